@@ -1,0 +1,187 @@
+/*
+ * kvc.h -- attention against a KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over four operations and two helpers.  Every pointer named
+ * "device" must point to memory on the current HIP device; the library never
+ * allocates, never frees, keeps no pointer after a call returns and has no
+ * global mutable state, so calls on different streams are independent.
+ * Every call is asynchronous on the given stream (a hipStream_t passed as
+ * void*, NULL for the default stream) and never synchronises the device.
+ *
+ * Cache layout (nanochat post, "What the KV cache looks like on disk"): K and
+ * V are each one contiguous array of shape
+ *     (n_layers, batch, max_seq, n_kv_heads, head_dim)
+ * in row-major order, and seqlens is an int32 array of shape (batch,) giving
+ * how many positions of each row are filled.  Under GQA the cache holds only
+ * the n_kv_heads key/value heads; query head h reads KV head
+ * h / (n_q_heads / n_kv_heads).  The library's kernels read seqlens and never
+ * change it (the clone excepted, which sets the destination's): as on that
+ * page, the caller advances it once per step, after every layer has run.
+ *
+ * Data types: q, out, k_new, v_new and the cache share one element type,
+ * KVC_F32 or KVC_BF16 (bfloat16, round to nearest even).  All accumulation
+ * is in float32.  head_dim must be 64 or 128.
+ *
+ * Errors.  A call first validates its arguments on the host; if that fails
+ * it returns a negative KVC_E_* code and launches nothing, so nothing is
+ * written.  Conditions that depend on device data (seqlens) are checked by
+ * the kernels: the offending batch row is skipped -- nothing is written for
+ * it -- and the matching KVC_DEV_* bit is OR-ed into *dev_err, a device int32
+ * the caller owns and reads after it next synchronises.  dev_err may be NULL,
+ * in which case those rows are still skipped but not reported.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, out, k_new, v_new and the cache. */
+enum { KVC_F32 = 0, KVC_BF16 = 1 };
+
+/* Host-side status codes (return values). */
+enum {
+  KVC_OK = 0,
+  KVC_E_ARG = -1,       /* null pointer, T < 1, layer out of range, bad scale or split size */
+  KVC_E_SHAPE = -2,     /* n_q_heads % n_kv_heads != 0, unsupported head_dim, descriptor mismatch */
+  KVC_E_CAPACITY = -3,  /* clone: dst.max_seq < src.max_seq, or src_len outside [0, src.max_seq] */
+  KVC_E_DTYPE = -4,     /* unknown element type, or source and destination types differ */
+  KVC_E_WORKSPACE = -5, /* decode workspace missing or smaller than kvc_decode_workspace_bytes */
+  KVC_E_LAUNCH = -6     /* a HIP launch failed */
+};
+
+/* Device-side error bits OR-ed into *dev_err. */
+enum {
+  KVC_DEV_CAPACITY = 1,  /* seqlens[b] < 0, or seqlens[b] + T > max_seq: row b skipped */
+  KVC_DEV_NOT_EMPTY = 2, /* clone: destination row b had seqlens[b] != 0: row b skipped */
+  KVC_DEV_SRC_LEN = 4    /* clone: source seqlens[0] != src_len: nothing copied */
+};
+
+/* Describes caller-owned device buffers; the library only reads the struct. */
+typedef struct kvc_cache {
+  void* k;          /* device, (n_layers, batch, max_seq, n_kv_heads, head_dim) */
+  void* v;          /* device, same shape as k */
+  int32_t* seqlens; /* device, (batch,) */
+  int32_t n_layers;
+  int32_t batch;
+  int32_t max_seq;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;    /* KVC_F32 or KVC_BF16 */
+} kvc_cache;
+
+/*
+ * kvc_rope_append -- rotate new q and k at each row's own position offset
+ * and write the new k and v in place into layer `layer` of the cache.
+ *
+ * Tiny-GPT post, "Two Gotchas That Break It Quietly", Gotcha 1: a cached
+ * step rotates its tokens at positions start .. start+T-1, where start is the
+ * row's offset, with angles f32(f32(p) * inv_freq[i]), inv_freq[i] =
+ * rope_base^(-2i/head_dim) (rounded once to float32), dimension i paired
+ * with i + head_dim/2.  "The Cache, in Code": the rotated q and k are cast to
+ * the value type and the rotated k is what the cache keeps.  nanochat post,
+ * "What the KV cache looks like on disk": the new K/V slices are written in
+ * place at each row's cache_seqlens offset.
+ *
+ *   q      device, (batch, T, n_q_heads, head_dim), raw (unrotated) queries.
+ *   q_out  device, same shape; receives the rotated queries.  May equal q.
+ *   k_new  device, (batch, T, n_kv_heads, head_dim), raw keys.
+ *   v_new  device, (batch, T, n_kv_heads, head_dim), values (copied bit for bit).
+ *
+ * For row b with P = seqlens[b], token t goes to position P + t:
+ *   K[layer, b, P+t] = round(rotate(k_new[b, t], P+t)),  V[layer, b, P+t] = v_new[b, t],
+ *   q_out[b, t] = round(rotate(q[b, t], P+t)).
+ * Nothing else in the cache is written and seqlens is not changed.  A row with
+ * P < 0 or P + T > max_seq is skipped entirely (KVC_DEV_CAPACITY), q_out included.
+ */
+int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* q_out,
+                    const void* k_new, const void* v_new, int32_t T, int32_t n_q_heads,
+                    float rope_base, int32_t* dev_err, void* stream);
+
+/*
+ * kvc_decode_workspace_bytes -- size of the float32 scratch kvc_attn_decode
+ * needs for split-KV partial results with this cache, head count and split
+ * size (split_keys 0 = the library default).  Pure host function; returns 0
+ * for an invalid descriptor.
+ */
+size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int32_t split_keys);
+
+/*
+ * kvc_attn_decode -- one query token per row against the whole cached
+ * prefix of layer `layer`, after its k/v were appended.
+ *
+ * Tiny-GPT post, Gotcha 2: a single decode query sees every cached key
+ * (no causal mask).  nanochat post: attention runs against the full cache,
+ * with GQA head sharing.  Cake paper, Section 3: softmax(q K^T * scale) V,
+ * scale = 1/sqrt(head_dim) (the default of the post's attention call).
+ *
+ *   q_rot  device, (batch, 1, n_q_heads, head_dim), rotated queries (q_out of
+ *          kvc_rope_append).
+ *   out    device, same shape as q_rot.
+ *   scale  softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *   split_keys  keys per split-KV work unit: 0 = default, else a positive
+ *          multiple of 64.  Results for a row depend only on its length, the
+ *          split size and the shapes, never on the batch size or other rows.
+ *   workspace   device scratch of at least kvc_decode_workspace_bytes bytes,
+ *          owned by the caller, clobbered by the call.
+ *
+ * For row b with P = seqlens[b], keys 0..P (P+1 of them, the new token's
+ * included) are attended.  Rows with P < 0 or P + 1 > max_seq are skipped
+ * (KVC_DEV_CAPACITY) and their out is not written.
+ */
+int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out,
+                    int32_t n_q_heads, float scale, int32_t split_keys, void* workspace,
+                    size_t workspace_bytes, int32_t* dev_err, void* stream);
+
+/*
+ * kvc_attn_prefill -- T new query tokens per row, causal by absolute position,
+ * against layer `layer` of the cache after their k/v were appended.
+ *
+ * Tiny-GPT post, Gotcha 2 (causal mask for a multi-token prompt) and Cake
+ * paper, Section 3 "Chunk Prefill" (each chunk attends to every earlier
+ * token): query t of row b sits at position P + t, P = seqlens[b], and sees
+ * keys 0..P+t.  P = 0 is a one-shot prefill; P > 0 a later chunk.  bfloat16
+ * runs on MFMA matrix cores (float32 accumulation, probabilities rounded to
+ * bfloat16 for the P*V product); float32 runs on vector ALUs.
+ *
+ *   q_rot  device, (batch, T, n_q_heads, head_dim), rotated queries.
+ *   out    device, same shape.
+ *   scale  softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *
+ * Rows with P < 0 or P + T > max_seq are skipped (KVC_DEV_CAPACITY).
+ */
+int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out,
+                     int32_t T, int32_t n_q_heads, float scale, int32_t* dev_err, void* stream);
+
+/*
+ * kvc_prefill_clone -- copy a batch-1 prefill into every row of an empty
+ * batch-N cache (nanochat post, "The prefill trick, 12 lines").
+ *
+ * Preconditions, from the post's asserts: the destination is empty, both
+ * caches have the same n_layers, n_kv_heads and head_dim (the post's n_heads
+ * read as the cache's KV-head axis) and element type, and dst->max_seq >=
+ * src->max_seq; src->batch must be 1.  src_len is the host-known number of
+ * filled source positions (the post's other.get_pos()); it must equal
+ * src->seqlens[0] on the device.
+ *
+ * For every layer and every destination row b with dst seqlens[b] == 0:
+ *   dst K/V[layer, b, 0:src_len] = src K/V[layer, 0, 0:src_len], then dst seqlens[b] = src_len.
+ * Destination positions >= src_len are not touched.  A row with
+ * seqlens[b] != 0 is skipped (KVC_DEV_NOT_EMPTY); if src seqlens[0] !=
+ * src_len nothing at all is written (KVC_DEV_SRC_LEN).
+ */
+int kvc_prefill_clone(const kvc_cache* src, int32_t src_len, const kvc_cache* dst,
+                      int32_t* dev_err, void* stream);
+
+/* A static, human-readable string for a KVC_OK / KVC_E_* status. */
+const char* kvc_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,203 @@
+// The C entry points of libkvc: validate on the host, then launch on the
+// caller's stream.  Nothing here allocates, synchronises or keeps state.
+#include <math.h>
+#include <stdint.h>
+
+#include "kvc.h"
+#include "kvc_launch.h"
+
+namespace {
+
+constexpr int32_t kDefaultSplitKeys = 512;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_cache(const kvc_cache* c) {
+  if (!c || !c->k || !c->v || !c->seqlens) return KVC_E_ARG;
+  if (!aligned16(c->k) || !aligned16(c->v) || (reinterpret_cast<uintptr_t>(c->seqlens) & 3u)) return KVC_E_ARG;
+  if (c->dtype != KVC_F32 && c->dtype != KVC_BF16) return KVC_E_DTYPE;
+  if (c->n_layers < 1 || c->batch < 1 || c->max_seq < 1 || c->n_kv_heads < 1) return KVC_E_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return KVC_E_SHAPE;
+  return KVC_OK;
+}
+
+int check_heads(const kvc_cache* c, int32_t n_q_heads) {
+  if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0) return KVC_E_SHAPE;
+  return KVC_OK;
+}
+
+kvc::LayerView layer_view(const kvc_cache* c, int32_t layer) {
+  const size_t esz = c->dtype == KVC_BF16 ? 2 : 4;
+  const size_t layer_bytes = size_t(c->batch) * c->max_seq * c->n_kv_heads * c->head_dim * esz;
+  kvc::LayerView v;
+  v.k = static_cast<uint8_t*>(c->k) + size_t(layer) * layer_bytes;
+  v.v = static_cast<uint8_t*>(c->v) + size_t(layer) * layer_bytes;
+  v.seqlens = c->seqlens;
+  v.batch = c->batch;
+  v.max_seq = c->max_seq;
+  v.n_kv_heads = c->n_kv_heads;
+  v.head_dim = c->head_dim;
+  v.dtype = c->dtype;
+  return v;
+}
+
+bool resolve_scale(float scale, int32_t head_dim, float* out) {
+  if (isnan(scale) || isinf(scale)) return false;
+  *out = scale > 0.f ? scale : float(1.0 / sqrt(double(head_dim)));
+  return true;
+}
+
+int32_t resolve_split(int32_t split_keys) { return split_keys == 0 ? kDefaultSplitKeys : split_keys; }
+
+size_t decode_ws_bytes(const kvc_cache* c, int32_t n_q_heads, int32_t split_keys) {
+  const int32_t sk = resolve_split(split_keys);
+  const int64_t max_splits = (int64_t(c->max_seq) + sk - 1) / sk;
+  if (max_splits <= 1) return 0;  // every row fits one split: written directly
+  return size_t(c->batch) * size_t(n_q_heads) * size_t(max_splits) * size_t(c->head_dim + 2) * sizeof(float);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* q_out, const void* k_new,
+                    const void* v_new, int32_t T, int32_t n_q_heads, float rope_base, int32_t* dev_err,
+                    void* stream) {
+  int st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (layer < 0 || layer >= cache->n_layers || T < 1) return KVC_E_ARG;
+  if (!q || !q_out || !k_new || !v_new) return KVC_E_ARG;
+  if (!aligned16(q) || !aligned16(q_out) || !aligned16(k_new) || !aligned16(v_new)) return KVC_E_ARG;
+  if (!(rope_base > 1.f) || isinf(rope_base)) return KVC_E_ARG;
+  if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
+  if (int64_t(cache->batch) * T > 0x7fffffffLL) return KVC_E_ARG;
+  kvc::RopeAppendParams p;
+  p.kv = layer_view(cache, layer);
+  p.q = q;
+  p.q_out = q_out;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.T = T;
+  p.n_q_heads = n_q_heads;
+  // inv_freq[i] = base^(-2i/D): evaluated in double, rounded once to float.
+  for (int i = 0; i < 64; ++i)
+    p.inv_freq[i] = i < cache->head_dim / 2 ? float(pow(double(rope_base), -2.0 * i / cache->head_dim)) : 0.f;
+  p.dev_err = dev_err;
+  return launch_status(kvc::launch_rope_append(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int32_t split_keys) {
+  if (check_cache(cache) != KVC_OK || check_heads(cache, n_q_heads) != KVC_OK) return 0;
+  if (split_keys < 0 || split_keys % 64 != 0) return 0;
+  return decode_ws_bytes(cache, n_q_heads, split_keys);
+}
+
+int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out, int32_t n_q_heads,
+                    float scale, int32_t split_keys, void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                    void* stream) {
+  int st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (layer < 0 || layer >= cache->n_layers) return KVC_E_ARG;
+  if (!q_rot || !out || !aligned16(q_rot) || !aligned16(out)) return KVC_E_ARG;
+  if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
+  if (split_keys < 0 || split_keys % 64 != 0) return KVC_E_ARG;
+  kvc::SplitParams p;
+  if (!resolve_scale(scale, cache->head_dim, &p.scale_log2)) return KVC_E_ARG;
+  p.scale_log2 *= 1.4426950408889634f;
+  const int32_t sk = resolve_split(split_keys);
+  const size_t need = decode_ws_bytes(cache, n_q_heads, split_keys);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return KVC_E_WORKSPACE;
+  p.kv = layer_view(cache, layer);
+  p.q = q_rot;
+  p.out = out;
+  p.T = 1;
+  p.n_q_heads = n_q_heads;
+  p.split_keys = sk;
+  p.max_splits = int32_t((int64_t(cache->max_seq) + sk - 1) / sk);
+  p.direct = need == 0;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.direct ? nullptr
+                     : p.ws_o + size_t(cache->batch) * n_q_heads * size_t(p.max_splits) * cache->head_dim;
+  p.dev_err = dev_err;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = kvc::launch_split_attention(p, s);
+  if (e == hipSuccess && !p.direct) e = kvc::launch_split_combine(p, s);
+  return launch_status(e);
+}
+
+int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out, int32_t T,
+                     int32_t n_q_heads, float scale, int32_t* dev_err, void* stream) {
+  int st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (layer < 0 || layer >= cache->n_layers || T < 1) return KVC_E_ARG;
+  if (!q_rot || !out || !aligned16(q_rot) || !aligned16(out)) return KVC_E_ARG;
+  if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
+  float sc;
+  if (!resolve_scale(scale, cache->head_dim, &sc)) return KVC_E_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->dtype == KVC_BF16) {
+    kvc::PrefillParams p;
+    p.kv = layer_view(cache, layer);
+    p.q = q_rot;
+    p.out = out;
+    p.T = T;
+    p.n_q_heads = n_q_heads;
+    p.scale_log2 = sc * 1.4426950408889634f;
+    p.dev_err = dev_err;
+    return launch_status(kvc::launch_prefill_mfma(p, s));
+  }
+  // float32: one split spanning the whole cache per query row, written directly.
+  kvc::SplitParams p;
+  p.kv = layer_view(cache, layer);
+  p.q = q_rot;
+  p.out = out;
+  p.T = T;
+  p.n_q_heads = n_q_heads;
+  p.split_keys = int32_t((int64_t(cache->max_seq) + 63) / 64 * 64);
+  p.max_splits = 1;
+  p.direct = 1;
+  p.ws_o = nullptr;
+  p.ws_ml = nullptr;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.dev_err = dev_err;
+  return launch_status(kvc::launch_split_attention(p, s));
+}
+
+int kvc_prefill_clone(const kvc_cache* src, int32_t src_len, const kvc_cache* dst, int32_t* dev_err,
+                      void* stream) {
+  int st = check_cache(src);
+  if (st != KVC_OK) return st;
+  if ((st = check_cache(dst)) != KVC_OK) return st;
+  if (src->dtype != dst->dtype) return KVC_E_DTYPE;
+  if (src->batch != 1) return KVC_E_SHAPE;
+  if (src->n_layers != dst->n_layers || src->n_kv_heads != dst->n_kv_heads || src->head_dim != dst->head_dim)
+    return KVC_E_SHAPE;
+  if (dst->max_seq < src->max_seq) return KVC_E_CAPACITY;
+  if (src_len < 0 || src_len > src->max_seq) return KVC_E_CAPACITY;
+  if (src->n_layers > 65535) return KVC_E_SHAPE;
+  kvc::CloneParams p;
+  p.src = layer_view(src, 0);
+  p.dst = layer_view(dst, 0);
+  p.dst_seqlens = dst->seqlens;
+  p.n_layers = src->n_layers;
+  p.src_len = src_len;
+  p.dev_err = dev_err;
+  return launch_status(kvc::launch_clone(p, static_cast<hipStream_t>(stream)));
+}
+
+const char* kvc_status_string(int status) {
+  switch (status) {
+    case KVC_OK: return "ok";
+    case KVC_E_ARG: return "invalid argument (null or misaligned pointer, T < 1, layer out of range, bad scale/base/split)";
+    case KVC_E_SHAPE: return "unsupported or mismatched shape (head_dim not 64/128, n_q_heads % n_kv_heads, descriptor mismatch)";
+    case KVC_E_CAPACITY: return "capacity (clone destination max_seq smaller than source, or src_len out of range)";
+    case KVC_E_DTYPE: return "unsupported or mismatched element type";
+    case KVC_E_WORKSPACE: return "decode workspace missing, misaligned or too small";
+    case KVC_E_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

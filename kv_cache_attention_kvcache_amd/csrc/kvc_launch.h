@@ -1,0 +1,69 @@
+// Host-side launchers of the kvc kernels.  The C entry points validate their
+// arguments and then call exactly one of these; every launcher returns the
+// hipError_t of its last launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvc {
+
+// One layer of a cache: element pointers already offset to that layer.
+struct LayerView {
+  void* k;
+  void* v;
+  const int32_t* seqlens;
+  int32_t batch, max_seq, n_kv_heads, head_dim, dtype;
+};
+
+struct RopeAppendParams {
+  LayerView kv;
+  const void* q;
+  void* q_out;
+  const void* k_new;
+  const void* v_new;
+  int32_t T, n_q_heads;
+  float inv_freq[64];  // float32 frequencies, head_dim / 2 of them
+  int32_t* dev_err;
+};
+hipError_t launch_rope_append(const RopeAppendParams& p, hipStream_t s);
+
+// Split-KV attention over rows (b, t): row b's query t attends to keys 0..seqlens[b]+t.
+// Decode is T = 1.  With one split per row ("direct") the output is written
+// straight away; otherwise float32 partials go to the workspace and
+// launch_split_combine folds them.
+struct SplitParams {
+  LayerView kv;
+  const void* q;
+  void* out;
+  float* ws_o;   // (batch*T, n_q_heads, max_splits, head_dim)
+  float* ws_ml;  // (batch*T, n_q_heads, max_splits, 2): running max (log2 units) and sum
+  int32_t T, n_q_heads, split_keys, max_splits;
+  float scale_log2;  // softmax scale * log2(e)
+  int32_t direct;
+  int32_t* dev_err;
+};
+hipError_t launch_split_attention(const SplitParams& p, hipStream_t s);
+hipError_t launch_split_combine(const SplitParams& p, hipStream_t s);
+
+struct PrefillParams {
+  LayerView kv;
+  const void* q;
+  void* out;
+  int32_t T, n_q_heads;
+  float scale_log2;
+  int32_t* dev_err;
+};
+hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t s);
+
+struct CloneParams {
+  LayerView src;  // layer 0 view; n_layers below
+  LayerView dst;
+  int32_t* dst_seqlens;
+  int32_t n_layers, src_len;
+  int32_t* dev_err;
+};
+hipError_t launch_clone(const CloneParams& p, hipStream_t s);
+
+}  // namespace kvc

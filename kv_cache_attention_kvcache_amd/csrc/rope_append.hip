@@ -1,0 +1,120 @@
+// Fused RoPE + in-place K/V append (one token row per workgroup).
+//
+// Tiny-GPT post, "Two Gotchas That Break It Quietly" (Gotcha 1): new tokens
+// are rotated at positions offset by the row's start, with a float32 angle
+// table.  nanochat post, "What the KV cache looks like on disk": the new K/V
+// slices are written in place at each row's cache_seqlens offset.
+//
+// Element-wise and HBM-bound: per token it reads (Hq + 2 Hkv) head vectors
+// and writes the same amount.  A workgroup takes one (row, token): it
+// evaluates cos/sin of the token's head_dim/2 angles once into LDS, then
+// rotates every q head and k head with 4-pair vectors and copies v with
+// 16-byte vectors.
+#include "kvc_device.h"
+#include "kvc_launch.h"
+#include "kvc.h"
+
+namespace kvc {
+
+template <typename T>
+struct Vec4;  // four consecutive elements <-> float
+
+template <>
+struct Vec4<float> {
+  static __device__ __forceinline__ void load(const float* p, float* x) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float* x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+
+template <>
+struct Vec4<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float* x) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* x) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendParams p) {
+  constexpr int HALF = D / 2;
+  constexpr int QUADS = HALF / 4;  // 4-pair groups per head vector
+  __shared__ __align__(16) float cs[HALF];
+  __shared__ __align__(16) float sn[HALF];
+
+  const int row = blockIdx.x;  // b * T + t
+  const int b = row / p.T;
+  const int t = row - b * p.T;
+  const int start = p.kv.seqlens[b];
+  if (start < 0 || start > p.kv.max_seq - p.T) {
+    if (t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
+    return;
+  }
+  const int pos = start + t;
+  if (threadIdx.x < HALF) {
+    // One float32 product, as the angle table is built; full-range sincos.
+    const float theta = __fmul_rn(static_cast<float>(pos), p.inv_freq[threadIdx.x]);
+    float s, c;
+    sincosf(theta, &s, &c);
+    cs[threadIdx.x] = c;
+    sn[threadIdx.x] = s;
+  }
+  __syncthreads();
+
+  const int hq = p.n_q_heads;
+  const int hkv = p.kv.n_kv_heads;
+  const T* q_row = static_cast<const T*>(p.q) + size_t(row) * hq * D;
+  T* q_out_row = static_cast<T*>(p.q_out) + size_t(row) * hq * D;
+  const T* k_row = static_cast<const T*>(p.k_new) + size_t(row) * hkv * D;
+  const size_t slot = (size_t(b) * p.kv.max_seq + pos) * hkv * D;
+  T* k_slot = static_cast<T*>(p.kv.k) + slot;
+
+  const int n_items = (hq + hkv) * QUADS;
+  for (int it = threadIdx.x; it < n_items; it += blockDim.x) {
+    const int head = it / QUADS;
+    const int i0 = (it - head * QUADS) * 4;
+    const T* src = head < hq ? q_row + head * D : k_row + (head - hq) * D;
+    T* dst = head < hq ? q_out_row + head * D : k_slot + (head - hq) * D;
+    float a[4], b2[4], ra[4], rb[4];
+    Vec4<T>::load(src + i0, a);
+    Vec4<T>::load(src + i0 + HALF, b2);
+    const float4 c4 = *reinterpret_cast<const float4*>(&cs[i0]);
+    const float4 s4 = *reinterpret_cast<const float4*>(&sn[i0]);
+    const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+    const float s[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = a[j] * c[j] - b2[j] * s[j];
+      rb[j] = a[j] * s[j] + b2[j] * c[j];
+    }
+    Vec4<T>::store(dst + i0, ra);
+    Vec4<T>::store(dst + i0 + HALF, rb);
+  }
+
+  // v: a bit copy into the slot.
+  const uint4* v_src = reinterpret_cast<const uint4*>(static_cast<const T*>(p.v_new) + size_t(row) * hkv * D);
+  uint4* v_dst = reinterpret_cast<uint4*>(static_cast<T*>(p.kv.v) + slot);
+  const int n_vec = hkv * D * int(sizeof(T)) / 16;
+  for (int it = threadIdx.x; it < n_vec; it += blockDim.x) v_dst[it] = v_src[it];
+}
+
+hipError_t launch_rope_append(const RopeAppendParams& p, hipStream_t s) {
+  const dim3 grid(p.kv.batch * p.T);
+  const dim3 block(256);
+  if (p.kv.dtype == KVC_BF16) {
+    if (p.kv.head_dim == 128) hipLaunchKernelGGL((rope_append_kernel<bf16_t, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((rope_append_kernel<bf16_t, 64>), grid, block, 0, s, p);
+  } else {
+    if (p.kv.head_dim == 128) hipLaunchKernelGGL((rope_append_kernel<float, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((rope_append_kernel<float, 64>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvc

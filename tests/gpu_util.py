@@ -1,0 +1,56 @@
+"""Helpers for GPU tests: moving seeded inputs to the device, poison fills, ulp distances."""
+import numpy as np
+import torch
+
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+NAN_BITS = {"f32": 0x7FC00000, "bf16": 0x7FC0}
+
+
+def dev(x: np.ndarray, dtype: str) -> torch.Tensor:
+    """float32/float64 numpy -> device tensor of the storage type (torch's RNE cast)."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(TORCH_DTYPE[dtype]).cuda()
+
+
+def host64(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> float64 numpy (exact for bf16 and f32)."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def poisoned(shape, dtype: str) -> torch.Tensor:
+    """A device tensor every element of which is a quiet NaN."""
+    if dtype == "bf16":
+        return torch.full(shape, NAN_BITS["bf16"], dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    return torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bit patterns as int64 numpy (for bit-exact comparisons)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().astype(np.int64) & 0xFFFF
+    return t.view(torch.int32).cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray, dtype: str) -> np.ndarray:
+    """|a - b| in units in the last place of the storage type (a, b float64 holding storage values)."""
+    if dtype == "bf16":
+        ia = (a.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
+        ib = (b.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
+        sign = 0x8000
+    else:
+        ia = a.astype(np.float32).view(np.uint32).astype(np.int64)
+        ib = b.astype(np.float32).view(np.uint32).astype(np.int64)
+        sign = 0x80000000
+    # map sign-magnitude to a monotonic integer line
+    ia = np.where(ia & sign, -(ia & (sign - 1)), ia)
+    ib = np.where(ib & sign, -(ib & (sign - 1)), ib)
+    return np.abs(ia - ib)
+
+
+def make_cache(kvc, n_layers, batch, max_seq, n_kv, d, dtype: str, poison=True):
+    shape = (n_layers, batch, max_seq, n_kv, d)
+    if poison:
+        k, v = poisoned(shape, dtype), poisoned(shape, dtype)
+    else:
+        k = torch.zeros(shape, dtype=TORCH_DTYPE[dtype], device="cuda")
+        v = torch.zeros(shape, dtype=TORCH_DTYPE[dtype], device="cuda")
+    return kvc.KVCache(k, v, torch.zeros(batch, dtype=torch.int32, device="cuda"))

@@ -1,0 +1,130 @@
+"""The C ABI on the host (CPU only): every declared symbol is exported, and
+argument validation rejects bad calls before anything is launched.
+
+None of these calls reaches the GPU: each one fails host validation (or is a
+pure host query), so they run on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "kv_cache_attention_kvcache_amd", "libkvc.so")
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):  # build once if nothing is built yet
+        import __graft_entry__
+
+        __graft_entry__._build_module().build()
+    import kv_cache_attention_kvcache_amd as kvc
+
+    return kvc
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(kvc_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    assert _declared() == sorted(["kvc_rope_append", "kvc_decode_workspace_bytes", "kvc_attn_decode",
+                                  "kvc_attn_prefill", "kvc_prefill_clone", "kvc_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert set(_declared()) == set(lib.EXPORTS)
+
+
+def _desc(lib, **kw):
+    d = dict(k=0x10000, v=0x20000, seqlens=0x30000, n_layers=2, batch=3, max_seq=100, n_kv_heads=4,
+             head_dim=128, dtype=lib.KVC_BF16)
+    d.update(kw)
+    return lib.kvc_cache(d["k"], d["v"], d["seqlens"], d["n_layers"], d["batch"], d["max_seq"],
+                         d["n_kv_heads"], d["head_dim"], d["dtype"])
+
+
+P = ctypes.c_void_p
+
+
+def test_status_strings(lib):
+    for code in range(-6, 1):
+        s = lib.kvc_status_string(code)
+        assert s and s != "unknown status"
+    assert lib.kvc_status_string(-99) == "unknown status"
+
+
+def test_workspace_query_is_a_host_function(lib):
+    d = _desc(lib, max_seq=4096, batch=8, head_dim=128)
+    n = lib.lib.kvc_decode_workspace_bytes(ctypes.byref(d), 16, 0)
+    assert n == 8 * 16 * 8 * (128 + 2) * 4  # 4096 / 512 = 8 splits of 512 keys
+    assert lib.lib.kvc_decode_workspace_bytes(ctypes.byref(d), 16, 64) == 8 * 16 * 64 * 130 * 4
+    assert lib.lib.kvc_decode_workspace_bytes(ctypes.byref(_desc(lib, max_seq=512)), 16, 0) == 0  # one split
+    assert lib.lib.kvc_decode_workspace_bytes(ctypes.byref(d), 6, 0) == 0  # 6 % 4 != 0: invalid
+    assert lib.lib.kvc_decode_workspace_bytes(ctypes.byref(d), 16, 100) == 0  # not a multiple of 64
+
+
+def test_rope_append_validation(lib):
+    L = lib.lib
+    d = _desc(lib)
+    good = dict(layer=0, q=P(0x40000), qo=P(0x40000), k=P(0x50000), v=P(0x60000), T=1, hq=16, base=10000.0)
+
+    def call(desc=d, **kw):
+        a = dict(good)
+        a.update(kw)
+        return L.kvc_rope_append(ctypes.byref(desc), a["layer"], a["q"], a["qo"], a["k"], a["v"], a["T"],
+                                 a["hq"], a["base"], None, None)
+
+    assert call(layer=2) == lib.KVC_E_ARG
+    assert call(layer=-1) == lib.KVC_E_ARG
+    assert call(T=0) == lib.KVC_E_ARG
+    assert call(q=None) == lib.KVC_E_ARG
+    assert call(k=P(0x50004)) == lib.KVC_E_ARG  # misaligned
+    assert call(base=0.0) == lib.KVC_E_ARG
+    assert call(hq=6) == lib.KVC_E_SHAPE
+    assert call(desc=_desc(lib, head_dim=96)) == lib.KVC_E_SHAPE
+    assert call(desc=_desc(lib, dtype=7)) == lib.KVC_E_DTYPE
+    assert call(desc=_desc(lib, k=0)) == lib.KVC_E_ARG
+    assert L.kvc_rope_append(None, 0, P(16), P(16), P(16), P(16), 1, 4, 1e4, None, None) == lib.KVC_E_ARG
+
+
+def test_decode_and_prefill_validation(lib):
+    L = lib.lib
+    d = _desc(lib, max_seq=4096)
+    q = P(0x40000)
+    assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 16, 0.0, 0, None, 0, None, None) == lib.KVC_E_WORKSPACE
+    assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 16, 0.0, 100, None, 0, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 16, float("nan"), 0, P(0x70000), 1 << 30, None,
+                             None) == lib.KVC_E_ARG
+    assert L.kvc_attn_decode(ctypes.byref(d), 5, q, q, 16, 0.0, 0, P(0x70000), 1 << 30, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 5, 0.0, 0, P(0x70000), 1 << 30, None, None) == lib.KVC_E_SHAPE
+    assert L.kvc_attn_prefill(ctypes.byref(d), 0, q, q, 0, 16, 0.0, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_prefill(ctypes.byref(d), 0, None, q, 4, 16, 0.0, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_prefill(ctypes.byref(_desc(lib, head_dim=32)), 0, q, q, 4, 16, 0.0, None,
+                              None) == lib.KVC_E_SHAPE
+
+
+def test_clone_validation(lib):
+    L = lib.lib
+    src = _desc(lib, batch=1, max_seq=100)
+    ok = _desc(lib, batch=8, max_seq=100)
+    assert L.kvc_prefill_clone(ctypes.byref(src), 10, ctypes.byref(_desc(lib, batch=8, max_seq=99)), None,
+                               None) == lib.KVC_E_CAPACITY
+    assert L.kvc_prefill_clone(ctypes.byref(src), 101, ctypes.byref(ok), None, None) == lib.KVC_E_CAPACITY
+    assert L.kvc_prefill_clone(ctypes.byref(src), -1, ctypes.byref(ok), None, None) == lib.KVC_E_CAPACITY
+    assert L.kvc_prefill_clone(ctypes.byref(_desc(lib, batch=2)), 10, ctypes.byref(ok), None,
+                               None) == lib.KVC_E_SHAPE
+    assert L.kvc_prefill_clone(ctypes.byref(src), 10, ctypes.byref(_desc(lib, batch=8, n_layers=3, max_seq=100)),
+                               None, None) == lib.KVC_E_SHAPE
+    assert L.kvc_prefill_clone(ctypes.byref(src), 10, ctypes.byref(_desc(lib, batch=8, n_kv_heads=8, max_seq=100)),
+                               None, None) == lib.KVC_E_SHAPE
+    assert L.kvc_prefill_clone(ctypes.byref(src), 10,
+                               ctypes.byref(_desc(lib, batch=8, max_seq=100, dtype=lib.KVC_F32)), None,
+                               None) == lib.KVC_E_DTYPE
