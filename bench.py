@@ -1,0 +1,262 @@
+"""Throughput of attention against a KV cache on one MI355X.
+
+One step = one pass of the whole hot path over the long-context workload
+(a 73,728-token random sequence, 64 q / 8 kv heads, head_dim 128, bf16):
+  1. chunked prefill: 18 chunks of 4096 tokens, each fused RoPE+append then
+     causal prefill attention over everything cached so far;
+  2. clone of the batch-1 cache into an empty batch-8 cache;
+  3. 512 decode steps at batch 1 and 512 at batch 8 (the cloned rows, each
+     with its own new tokens): per step RoPE+append, split-KV decode, and
+     the caller's seqlens += 1.
+All inputs are seeded, synthetic and resident in HBM before timing starts.
+
+Reported: decode attention K/V bytes per second (the JSON `value`), prefill
+attention TFLOP/s, tokens/s, a roofline record for the decode kernel pair
+(HIP events around every decode call, on the stream they run on) and the CPU
+oracle timed on a bounded sample of the same work.
+
+    python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--decode-steps", type=int, default=None, help="decode steps per batch size (default 512)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg, quiet=False):
+    if not quiet:
+        print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events around calls on the current stream; durations read after a sync."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __enter__(self):
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
+        self.e0.record()
+        return self
+
+    def __exit__(self, *a):
+        self.e1.record()
+        self.pairs.append((self.e0, self.e1))
+
+    def times_ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU "
+              "by design and every figure it reports is one GPU's.", file=sys.stderr)
+        sys.exit(2)
+    import kv_cache_attention_kvcache_amd as kvc
+    import synth
+
+    w = synth.LONG_CONTEXT
+    ctx, chunk = w.extra["context"], w.extra["chunk"]
+    n_chunks = ctx // chunk
+    n_dec = w.extra["steps"] if args.decode_steps is None else args.decode_steps
+    rows = w.extra["clone_rows"]
+    hq, hkv, d, max_seq = w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq
+    bf = torch.bfloat16
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q_ = args.quiet
+
+    # ---------------- inputs (seeded, resident on the device before timing)
+    t0 = time.time()
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(bf).to(dev)
+    pq, pk, pv = [], [], []
+    for c in range(n_chunks):
+        q, k, v = synth.chunk_qkv(w, c, chunk)
+        pq.append(to_dev(q[None]))
+        pk.append(to_dev(k[None]))
+        pv.append(to_dev(v[None]))
+    dq = {1: [], rows: []}
+    dk = {1: [], rows: []}
+    dv = {1: [], rows: []}
+    for s in range(n_dec):
+        q, k, v = synth.decode_qkv_batch(w, s, rows)
+        for b, sl in ((1, slice(0, 1)), (rows, slice(0, rows))):
+            dq[b].append(to_dev(q[sl]))
+            dk[b].append(to_dev(k[sl]))
+            dv[b].append(to_dev(v[sl]))
+    log(f"inputs ready in {time.time() - t0:.1f}s", q_)
+
+    cache1 = kvc.KVCache.empty(1, 1, max_seq, hkv, d, dtype=bf, device=dev)
+    cache8 = kvc.KVCache.empty(1, rows, max_seq, hkv, d, dtype=bf, device=dev)
+    ws = torch.empty(max(kvc.kvc_decode_workspace_bytes(cache8, hq), kvc.kvc_decode_workspace_bytes(cache1, hq)),
+                     dtype=torch.uint8, device=dev)
+    qrot_p = torch.empty((1, chunk, hq, d), dtype=bf, device=dev)
+    out_p = torch.empty_like(qrot_p)
+    qrot_d = {b: torch.empty((b, 1, hq, d), dtype=bf, device=dev) for b in (1, rows)}
+    out_d = {b: torch.empty((b, 1, hq, d), dtype=bf, device=dev) for b in (1, rows)}
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    t_pre, t_clone, t_dec = Timer(), Timer(), {1: Timer(), rows: Timer()}
+    phase = {k: Timer() for k in ("prefill", "clone", "decode1", "decode8")}
+
+    def step(timed: bool):
+        cache1.seqlens.zero_()
+        cache8.seqlens.zero_()
+        with phase["prefill"] if timed else _Null():
+            for c in range(n_chunks):
+                kvc.kvc_rope_append(cache1, 0, pq[c], pk[c], pv[c], q_out=qrot_p, dev_err=err)
+                with t_pre if timed else _Null():
+                    kvc.kvc_attn_prefill(cache1, 0, qrot_p, out=out_p, dev_err=err)
+                cache1.seqlens += chunk
+        with phase["clone"] if timed else _Null():
+            with t_clone if timed else _Null():
+                kvc.kvc_prefill_clone(cache1, ctx, cache8, dev_err=err)
+        for b, cache in ((1, cache1), (rows, cache8)):
+            with phase["decode1" if b == 1 else "decode8"] if timed else _Null():
+                for s in range(n_dec):
+                    kvc.kvc_rope_append(cache, 0, dq[b][s], dk[b][s], dv[b][s], q_out=qrot_d[b], dev_err=err)
+                    with t_dec[b] if timed else _Null():
+                        kvc.kvc_attn_decode(cache, 0, qrot_d[b], out=out_d[b], workspace=ws, dev_err=err)
+                    cache.seqlens += 1
+
+    for i in range(args.warmup):
+        step(False)
+        torch.cuda.synchronize()
+        log(f"warmup step {i} done", q_)
+    torch.cuda.synchronize()
+    t_start = time.time()
+    for i in range(args.steps):
+        step(True)
+        log(f"timed step {i} enqueued", q_)
+    torch.cuda.synchronize()
+    wall = time.time() - t_start
+    assert err.item() == 0, f"device error bits {err.item()}"
+
+    # ---------------- algorithmic work
+    kv_bytes_tok = 2 * hkv * d * 2  # K and V, bf16
+    dec_bytes = {1: sum((ctx + s + 1) * kv_bytes_tok for s in range(n_dec)),
+                 rows: rows * sum((ctx + s + 1) * kv_bytes_tok for s in range(n_dec))}
+    pairs = sum(chunk * (c * chunk) + chunk * (chunk + 1) // 2 for c in range(n_chunks))
+    pre_flops = 4 * d * hq * pairs
+    K = args.steps
+    ms_pre = sum(t_pre.times_ms())
+    ms_dec = {b: sum(t_dec[b].times_ms()) for b in (1, rows)}
+    dec_total_bytes = K * (dec_bytes[1] + dec_bytes[rows])
+    dec_gbps = dec_total_bytes / ((ms_dec[1] + ms_dec[rows]) * 1e-3) / 1e9
+    pre_tflops = K * pre_flops / (ms_pre * 1e-3) / 1e12
+    # dominant decode launch: batch 8 (2.4 GB of K/V per call)
+    per_launch_bytes = dec_bytes[rows] / n_dec
+    avg_launch_ms = ms_dec[rows] / (K * n_dec)
+    achieved = per_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
+    ph = {k: sum(v.times_ms()) / K for k, v in phase.items()}
+    tokens = ctx + n_dec * (1 + rows)
+    ms_step = wall * 1e3 / K
+    res = {
+        "metric": "KV-cache decode attn HBM GB/s (% of peak); prefill attn TFLOP/s",
+        "value": round(dec_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "context": ctx, "chunk": chunk, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": d, "decode_steps": n_dec, "decode_batches": [1, rows], "parallelism": "none"},
+        "decode_hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "decode_gbps_by_batch": {str(b): round(K * dec_bytes[b] / (ms_dec[b] * 1e-3) / 1e9, 1) for b in (1, rows)},
+        "prefill_tflops": round(pre_tflops, 1),
+        "prefill_mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+        "prefill_ms": round(ms_pre / K, 2),
+        "clone_gbps": round((ctx * kv_bytes_tok * (1 + rows)) / (sum(t_clone.times_ms()) / K * 1e-3) / 1e9, 1),
+        "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "phase_ms": {k: round(v, 3) for k, v in ph.items()},
+        "roofline": {"bound": "hbm", "kernel": "decode (split_attention_kernel + split_combine_kernel), batch 8",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(per_launch_bytes), "avg_launch_us": round(avg_launch_ms * 1e3, 2)},
+        "roofline_prefill": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": round(pre_tflops, 1),
+                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+                             "flops_per_step": int(pre_flops), "avg_launch_us": round(ms_pre / (K * n_chunks) * 1e3, 1)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, kv_bytes_tok, q_)
+    print(json.dumps(res), flush=True)
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
+def cpu_baseline(w, kv_bytes_tok, quiet):
+    """The oracle, as it is, on the host: no-cache decode of one token at the full
+    73,728-token context (every key re-rotated from its raw value, all 64 heads),
+    repeated until about 10 s have passed.  Rate in K/V bytes per second, like `value`."""
+    import synth
+    from oracle import attention as oatt
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    ctx = w.extra["context"]
+    ks, vs = [], []
+    for c in range(ctx // w.extra["chunk"]):
+        k, v = synth.chunk_kv(w, c, w.extra["chunk"])
+        ks.append(k)
+        vs.append(v)
+    qd, kd, vd = synth.decode_qkv(w, 0, 0)
+    k_all = np.concatenate(ks + [kd])
+    v_all = np.concatenate(vs + [vd])
+    q_all = np.zeros((ctx + 1, w.n_q_heads, w.head_dim), dtype=np.float32)
+    q_all[ctx] = qd[0]
+    n, t0 = 0, time.time()
+    while True:
+        oatt.nocache_outputs(q_all, k_all, v_all, [ctx], "bf16")
+        n += 1
+        if time.time() - t0 > 10.0 or n >= 20:
+            break
+    dt = time.time() - t0
+    bytes_per = (ctx + 1) * kv_bytes_tok
+    log(f"cpu baseline: {n} oracle decode calls in {dt:.1f}s", quiet)
+    return {"value": round(n * bytes_per / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} no-cache decode calls of one token at context {ctx + 1} (64 q / 8 kv heads, "
+                      f"all keys re-rotated from raw), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

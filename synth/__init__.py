@@ -166,6 +166,13 @@ def chunk_qkv(w: Workload, chunk: int, n_tokens: int):
     return qkv_tokens(w, n_tokens, _ROLE_CHUNK, chunk)
 
 
+def chunk_kv(w: Workload, chunk: int, n_tokens: int):
+    """Only k, v of prefill chunk ``chunk`` (the same arrays chunk_qkv returns)."""
+    d = w.head_dim
+    return (normal((n_tokens, w.n_kv_heads, d), 1.0, w.seed, _ROLE_NEW, 1, _ROLE_CHUNK, chunk),
+            normal((n_tokens, w.n_kv_heads, d), 1.0, w.seed, _ROLE_NEW, 2, _ROLE_CHUNK, chunk))
+
+
 def decode_qkv(w: Workload, step: int, row: int):
     """Raw q (1, Hq, D), k, v (1, Hkv, D) of decode step ``step`` for batch row ``row``."""
     return qkv_tokens(w, 1, _ROLE_STEP, step, row)

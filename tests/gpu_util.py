@@ -54,3 +54,20 @@ def make_cache(kvc, n_layers, batch, max_seq, n_kv, d, dtype: str, poison=True):
         k = torch.zeros(shape, dtype=TORCH_DTYPE[dtype], device="cuda")
         v = torch.zeros(shape, dtype=TORCH_DTYPE[dtype], device="cuda")
     return kvc.KVCache(k, v, torch.zeros(batch, dtype=torch.int32, device="cuda"))
+
+
+def rope_error_ok(got: np.ndarray, ref: np.ndarray, x_in: np.ndarray, dtype: str) -> bool:
+    """Is a rotated vector within the error a float32 rotation can have?
+
+    The kernel rotates in float32 with float32 cos/sin (each within an ulp),
+    so an output's error scales with the pair's length |(a, b)|, not with the
+    output itself (which may be tiny by cancellation).  Allowed: one ulp of
+    the storage type at the output, or 2^-20 |(a, b)|, whichever is larger.
+    x_in: the unrotated input (..., D) in storage precision.
+    """
+    half = x_in.shape[-1] // 2
+    pair = np.sqrt(x_in[..., :half] ** 2 + x_in[..., half:] ** 2)
+    pair = np.concatenate([pair, pair], axis=-1)
+    _, e = np.frexp(np.abs(ref))
+    ulp = np.ldexp(1.0, e - (8 if dtype == "bf16" else 24))
+    return bool(np.all(np.abs(got - ref) <= np.maximum(ulp, pair * 2.0 ** -20)))
