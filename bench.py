@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps per batch size (default 512)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, one plain device-to-device copy of this many MiB (a known-size "
+                         "kernel whose HBM counters calibrate the profiler's byte counts)")
     return ap.parse_args()
 
 
@@ -208,6 +211,14 @@ def main():
                              "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
                              "flops_per_step": int(pre_flops), "avg_launch_us": round(ms_pre / (K * n_chunks) * 1e3, 1)},
     }
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = n
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, kv_bytes_tok, q_)
     print(json.dumps(res), flush=True)
