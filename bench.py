@@ -202,7 +202,7 @@ def main():
         "clone_gbps": round((ctx * kv_bytes_tok * (1 + rows)) / (sum(t_clone.times_ms()) / K * 1e-3) / 1e9, 1),
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "phase_ms": {k: round(v, 3) for k, v in ph.items()},
-        "roofline": {"bound": "hbm", "kernel": "decode (split_attention_kernel + split_combine_kernel), batch 8",
+        "roofline": {"bound": "hbm", "kernel": "decode (decode_bf16_kernel + decode_bf16_combine_kernel), batch 8",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_launch": int(per_launch_bytes), "avg_launch_us": round(avg_launch_ms * 1e3, 2)},

@@ -3,8 +3,9 @@
  *
  * A C ABI over four operations and two helpers.  Every pointer named
  * "device" must point to memory on the current HIP device; the library never
- * allocates, never frees, keeps no pointer after a call returns and has no
- * global mutable state, so calls on different streams are independent.
+ * allocates, never frees and keeps no pointer after a call returns.  Its only
+ * state is a per-device cache of read-only device properties (CU count,
+ * kernel occupancy), so calls on different streams are independent.
  * Every call is asynchronous on the given stream (a hipStream_t passed as
  * void*, NULL for the default stream) and never synchronises the device.
  *
@@ -104,11 +105,12 @@ int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* 
 
 /*
  * kvc_decode_workspace_bytes -- size of the float32 scratch kvc_attn_decode
- * needs for split-KV partial results with this cache, head count and split
- * size (split_keys 0 = the library default).  Pure host function; returns 0
- * for an invalid descriptor.
+ * needs for its partial results with this cache, query-head count and worker
+ * count (n_workers 0 = the library default).  A host function: it may query
+ * the current HIP device's properties, and launches nothing.  Returns 0 for an
+ * invalid descriptor or when no scratch is needed.
  */
-size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int32_t split_keys);
+size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int32_t n_workers);
 
 /*
  * kvc_attn_decode -- one query token per row against the whole cached
@@ -123,18 +125,23 @@ size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int
  *          kvc_rope_append).
  *   out    device, same shape as q_rot.
  *   scale  softmax scale; <= 0 selects 1/sqrt(head_dim).
- *   split_keys  keys per split-KV work unit: 0 = default, else a positive
- *          multiple of 64.  Results for a row depend only on its length, the
- *          split size and the shapes, never on the batch size or other rows.
+ *   n_workers  bfloat16 caches: the number of workgroups the cached keys of
+ *          all rows are split evenly over (split-KV); 0 = as many as the
+ *          device runs at once.  Float32 caches use fixed 512-key splits and
+ *          ignore it.  A result depends on the lengths of all rows and on
+ *          n_workers only through the order of float32 additions; it is
+ *          bit-identical run to run for the same inputs and n_workers.
  *   workspace   device scratch of at least kvc_decode_workspace_bytes bytes,
  *          owned by the caller, clobbered by the call.
  *
  * For row b with P = seqlens[b], keys 0..P (P+1 of them, the new token's
  * included) are attended.  Rows with P < 0 or P + 1 > max_seq are skipped
- * (KVC_DEV_CAPACITY) and their out is not written.
+ * (KVC_DEV_CAPACITY) and their out is not written.  bfloat16 caches whose one
+ * head row (max_seq * n_kv_heads * head_dim elements) reaches 2^30 are
+ * rejected with KVC_E_SHAPE.
  */
 int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out,
-                    int32_t n_q_heads, float scale, int32_t split_keys, void* workspace,
+                    int32_t n_q_heads, float scale, int32_t n_workers, void* workspace,
                     size_t workspace_bytes, int32_t* dev_err, void* stream);
 
 /*

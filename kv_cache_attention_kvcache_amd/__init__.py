@@ -165,24 +165,26 @@ def kvc_rope_append(cache: KVCache, layer: int, q, k_new, v_new, q_out=None, rop
     return q_out
 
 
-def kvc_decode_workspace_bytes(cache: KVCache, n_q_heads: int, split_keys: int = 0) -> int:
-    return int(lib.kvc_decode_workspace_bytes(cache.desc(), int(n_q_heads), int(split_keys)))
+def kvc_decode_workspace_bytes(cache: KVCache, n_q_heads: int, n_workers: int = 0) -> int:
+    return int(lib.kvc_decode_workspace_bytes(cache.desc(), int(n_q_heads), int(n_workers)))
 
 
-def kvc_attn_decode(cache: KVCache, layer: int, q_rot, out=None, scale: float = 0.0, split_keys: int = 0,
+def kvc_attn_decode(cache: KVCache, layer: int, q_rot, out=None, scale: float = 0.0, n_workers: int = 0,
                     workspace=None, dev_err=None, stream=None):
-    """One query token per row against layer `layer`'s cached prefix (keys 0..seqlens[b]); returns out."""
+    """One query token per row against layer `layer`'s cached prefix (keys 0..seqlens[b]); returns out.
+
+    n_workers: workgroups the bfloat16 kernel balances the keys over (0 = fill the device)."""
     b, t, hq, d = q_rot.shape
     _like(q_rot, cache, (cache.batch, 1, hq, cache.head_dim), "q_rot")
     if out is None:
         out = torch.empty_like(q_rot)
     _like(out, cache, q_rot.shape, "out")
-    need = kvc_decode_workspace_bytes(cache, hq, split_keys)
+    need = kvc_decode_workspace_bytes(cache, hq, n_workers)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=cache.k.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kvc_attn_decode(cache.desc(), int(layer), _ptr(q_rot), _ptr(out), int(hq), float(scale),
-                             int(split_keys), _ptr(workspace), ws_bytes, _ptr(dev_err),
+                             int(n_workers), _ptr(workspace), ws_bytes, _ptr(dev_err),
                              _stream(stream, cache.k.device))
     _check("kvc_attn_decode", st)
     return out

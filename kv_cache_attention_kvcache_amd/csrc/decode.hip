@@ -380,20 +380,15 @@ hipError_t launch_split_d(const SplitParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_split_attention(const SplitParams& p, hipStream_t s) {
-  if (p.kv.dtype == KVC_BF16)
-    return p.kv.head_dim == 128 ? launch_split_d<bf16_t, 128>(p, s) : launch_split_d<bf16_t, 64>(p, s);
+  if (p.kv.dtype != KVC_F32) return hipErrorInvalidValue;  // bfloat16 decode has its own kernel
   return p.kv.head_dim == 128 ? launch_split_d<float, 128>(p, s) : launch_split_d<float, 64>(p, s);
 }
 
 hipError_t launch_split_combine(const SplitParams& p, hipStream_t s) {
   const dim3 grid(p.kv.batch * p.T * p.n_q_heads);
-  if (p.kv.dtype == KVC_BF16) {
-    if (p.kv.head_dim == 128) hipLaunchKernelGGL((split_combine_kernel<bf16_t, 128>), grid, dim3(kWave), 0, s, p);
-    else hipLaunchKernelGGL((split_combine_kernel<bf16_t, 64>), grid, dim3(kWave), 0, s, p);
-  } else {
-    if (p.kv.head_dim == 128) hipLaunchKernelGGL((split_combine_kernel<float, 128>), grid, dim3(kWave), 0, s, p);
-    else hipLaunchKernelGGL((split_combine_kernel<float, 64>), grid, dim3(kWave), 0, s, p);
-  }
+  if (p.kv.dtype != KVC_F32) return hipErrorInvalidValue;
+  if (p.kv.head_dim == 128) hipLaunchKernelGGL((split_combine_kernel<float, 128>), grid, dim3(kWave), 0, s, p);
+  else hipLaunchKernelGGL((split_combine_kernel<float, 64>), grid, dim3(kWave), 0, s, p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,608 @@
+// Split-KV flash-decode for bfloat16 caches, on vector ALUs (no MFMA).
+//
+// Tiny-GPT post, Gotcha 2: a decode query sees every cached key.  nanochat
+// post ("What the KV cache looks like on disk"): attention runs against the
+// full cache, with KV heads shared by groups of query heads (GQA).  Cake paper,
+// Section 3: decode is memory-bound -- here it moves about 8 flops per K/V byte
+// at a GQA group of 8 -- so nothing is reshaped into matrix-core work.
+//
+// Work partition.  A segment is (row b, KV head g, block hb of GB query heads
+// of its group); it holds ceil(L_b / 32) tiles of 32 keys, L_b = seqlens[b]+1.
+// All segments laid end to end form N tiles; the grid is persistent (as many
+// workgroups as the device holds at once) and workgroup w takes the tiles
+// [w N / P, (w+1) N / P) -- the same K/V bytes per workgroup whatever the
+// lengths, so batch 1 at 73K keys and batch 64 with ragged lengths balance
+// alike.  The range is cut into runs (its intersection with each segment);
+// the four waves of the workgroup take the tiles of a run in turn.  At the end
+// of a run the waves fold their softmax states in LDS; a run that is a whole
+// segment writes the normalised output, any other run a float32 partial
+// (unnormalised o, running max, sum).  A workgroup writes at most two partials
+// (its first run and its last), and the combine kernel folds them per segment.
+//
+// One 32-key tile, per wave:
+//   * K and V are read with coalesced 16-byte buffer loads, 16 lanes per
+//     256-byte row (8 per 128-byte row at head_dim 64).  The buffer's range
+//     check returns zeros for keys at or past L_b, so no lane reads a slot of
+//     the cache it must not.  The next tile of the wave is always in flight
+//     while the current one is computed.
+//   * Scores: each lane dots its 8 head dims of its K rows against those dims
+//     of all GB queries (v_dot2_f32_bf16), then a DPP transpose-reduction
+//     across the lanes of a row sums the partial dots and leaves every lane
+//     with complete scores of one query head for two or four keys.  The lanes
+//     load the queries in a lane-dependent head order so that every exchange
+//     is a single add with a DPP operand (no selects).
+//   * Softmax: exp2 of log2-scaled scores against a per-head running maximum
+//     that is raised lazily -- only when a score exceeds it by more than 2^8
+//     (a ballot), so most tiles skip the max reduction and the rescale.
+//   * P*V: probabilities go to LDS as bfloat16 key pairs; V goes to LDS as
+//     key-pair-packed dims; each lane then owns head_dim/64 output dims of all
+//     GB heads and accumulates with v_dot2_f32_bf16 (two keys per product).
+#include "kvc_device.h"
+#include "kvc_launch.h"
+#include "kvc.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr int kTileKeys = 32;   // keys per wave tile
+constexpr int kWaves = 4;       // waves per workgroup
+constexpr float kLazyLog2 = 8.f;  // probabilities may reach 2^8 before the max is raised
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D, int GB>
+struct Cfg {
+  static constexpr int LPR = D / 8;                 // lanes per K/V row (16 bytes each)
+  static constexpr int RPI = kWave / LPR;           // rows per load instruction (= row groups)
+  static constexpr int NR = kTileKeys / RPI;        // K/V rows (slots) per lane per tile
+  static constexpr int S = LPR == 16 ? 4 : 3;       // transpose-reduction steps
+  static constexpr int HB = GB == 8 ? 3 : 2;        // steps that split the head axis
+  static constexpr int NRK = NR >> (S - HB);        // rows a lane keeps after the reduction
+  static constexpr int NPK = NRK / 2;               // key pairs a lane keeps
+  static constexpr int DL = D / kWave;              // output dims per lane in P*V
+  static constexpr int NPAIR = kTileKeys / 2;       // key pairs per tile
+  static constexpr int kVBytes = NPAIR * D * 4;     // V tile, key-pair packed
+  static constexpr int kPBytes = NPAIR * GB * 4;    // probabilities, key-pair packed
+  static constexpr int kWaveLds = kVBytes + kPBytes;
+  static constexpr int kMergeBytes = kWaves * GB * (D + 2) * 4;
+  static constexpr int kLds = kWaves * kWaveLds > kMergeBytes ? kWaves * kWaveLds : kMergeBytes;
+  static_assert(NPK >= 1 && NR % 2 == 0, "tile shape");
+};
+
+// DPP control of reduction step k: lane x exchanges with x ^ m_k inside its row
+// group.  head_dim 128 (16-lane groups): m = 8 (row_ror:8), 7 (row_half_mirror),
+// 2, 1 (quad perms).  head_dim 64 (8-lane groups): 7, 2, 1.
+template <int LPR, int K>
+constexpr int step_ctrl() {
+  if constexpr (LPR == 16) return K == 0 ? 0x128 : K == 1 ? 0x141 : K == 2 ? 0x4E : 0xB1;
+  else return K == 0 ? 0x141 : K == 1 ? 0x4E : 0xB1;
+}
+template <int LPR, int K>
+constexpr int step_mask() {
+  if constexpr (LPR == 16) return K == 0 ? 8 : K == 1 ? 7 : K == 2 ? 2 : 1;
+  else return K == 0 ? 7 : K == 1 ? 2 : 1;
+}
+
+// gh: the linear map (over GF(2)) from a lane's index x within its row group
+// to the XOR applied to its query-head order.  It satisfies gh(m_k) = GB/2^(k+1)
+// for the head-splitting steps and gh(m_k) = 0 for the row-splitting ones, so
+// that the value a lane sends at every step is exactly the one its partner keeps.
+template <int LPR, int GB>
+__host__ __device__ constexpr int gh(int x) {
+  // images of the lane-index bits 0..3
+  constexpr int img128_8[4] = {0, 1, 3, 4};
+  constexpr int img128_4[4] = {0, 0, 1, 2};
+  constexpr int img64_8[3] = {1, 2, 7};
+  constexpr int img64_4[3] = {0, 1, 3};
+  int r = 0;
+  for (int bit = 0; bit < (LPR == 16 ? 4 : 3); ++bit) {
+    if ((x >> bit) & 1) {
+      if constexpr (LPR == 16) r ^= GB == 8 ? img128_8[bit] : img128_4[bit];
+      else r ^= GB == 8 ? img64_8[bit] : img64_4[bit];
+    }
+  }
+  return r;
+}
+
+// Lane (within row group 0) that holds the scores of head h after the reduction.
+template <int LPR, int GB>
+__host__ __device__ constexpr int lane_of_head(int h) {
+  for (int x = 0; x < LPR; ++x)
+    if (gh<LPR, GB>(x) == h) return x;
+  return 0;
+}
+
+template <int K>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), K, 0xf, 0xf, true));
+}
+
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0);
+}
+
+// Number of 32-key tiles of row b, or 0 if its length is out of range.
+__device__ __forceinline__ int row_tiles(const int32_t* seqlens, int b, int max_seq) {
+  const int p = seqlens[b];
+  if (p < 0 || p > max_seq - 1) return 0;
+  return (p + kTileKeys) / kTileKeys;  // ceil((p + 1) / 32)
+}
+
+// The value of lane 0, known to the compiler to be wave-uniform (an SGPR).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return uniform(x);
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Tiles of all segments (N) and the segment holding flattened tile t.
+struct SegPos {
+  int b, sr, nt, base;  // row, segment within row, tiles per segment of row b, first tile
+};
+
+__device__ int total_tiles(const DecodeParams& p, int lane) {
+  int n = 0;
+  for (int b0 = 0; b0 < p.kv.batch; b0 += kWave) {
+    const int b = b0 + lane;
+    n += wave_sum_i(b < p.kv.batch ? row_tiles(p.kv.seqlens, b, p.kv.max_seq) : 0);
+  }
+  return n * p.kv.n_kv_heads * p.n_hb;
+}
+
+__device__ SegPos find_segment(const DecodeParams& p, int t, int lane) {
+  const int spr = p.kv.n_kv_heads * p.n_hb;  // segments per row
+  int cum = 0;
+  for (int b0 = 0; b0 < p.kv.batch; b0 += kWave) {
+    const int b = b0 + lane;
+    const int nt = b < p.kv.batch ? row_tiles(p.kv.seqlens, b, p.kv.max_seq) : 0;
+    const int incl = wave_incl_scan_i(nt * spr, lane);
+    const int total = uniform(__shfl(incl, kWave - 1));
+    if (cum + total > t) {
+      const unsigned long long hit = __ballot(cum + incl > t);
+      const int first = __builtin_ctzll(hit);
+      SegPos s;
+      s.b = uniform(b0 + first);
+      s.nt = uniform(__shfl(nt, first));
+      const int row_base = uniform(cum + __shfl(incl, first) - s.nt * spr);
+      s.sr = (t - row_base) / s.nt;
+      s.base = row_base + s.sr * s.nt;
+      return s;
+    }
+    cum += total;
+  }
+  SegPos s = {0, 0, 0, 0};
+  return s;  // not reached for t < N
+}
+
+// Flattened tile index w N / P where workgroup w's range starts.
+__device__ __forceinline__ int range_begin(long long w, int n, int n_wg) { return int(w * n / n_wg); }
+
+template <int D, int GB>
+__global__ __launch_bounds__(kWaves * kWave, 2) void decode_bf16_kernel(DecodeParams p) {
+  using C = Cfg<D, GB>;
+  constexpr int LPR = C::LPR;
+  __shared__ __align__(16) uint8_t smem[C::kLds];
+
+  const int wave = uniform(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int x = lane % LPR;      // lane within its row group
+  const int rg = lane / LPR;     // row group
+  const int ghx = gh<LPR, GB>(x);
+
+  const int n_tiles = total_tiles(p, lane);
+  const int t_begin = range_begin(blockIdx.x, n_tiles, p.n_wg);
+  const int t_end = range_begin(blockIdx.x + 1LL, n_tiles, p.n_wg);
+  if (t_begin >= t_end) return;
+
+  const int hq = p.n_q_heads;
+  const int hkv = p.kv.n_kv_heads;
+  const int group = hq / hkv;
+  const int spr = hkv * p.n_hb;
+  const int row_bytes = hkv * D * 2;  // bytes between consecutive positions of one head
+  const float c = p.scale_log2;
+
+  uint8_t* vlds = smem + wave * C::kWaveLds;
+  uint32_t* plds = reinterpret_cast<uint32_t*>(vlds + C::kVBytes);
+
+  // Per-lane byte offset of slot s's row within a tile: row = 2 (s/2 * RPI + rg) + (s & 1).
+  const int lane_off = 2 * rg * row_bytes + x * 16;
+
+  SegPos seg = find_segment(p, t_begin, lane);
+  int t = t_begin;
+  bool first_run = true;
+  while (t < t_end) {
+    const int seg_end = seg.base + seg.nt;
+    const int run_end = min(t_end, seg_end);
+    const bool complete = t == seg.base && run_end == seg_end;
+    const int g = seg.sr / p.n_hb;
+    const int hb = seg.sr - g * p.n_hb;
+    const int L = p.kv.seqlens[seg.b] + 1;
+    const int j0 = t - seg.base, j1 = run_end - seg.base;  // local tiles of the run
+
+    // Segment bases (row b, position 0, KV head g).
+    const size_t elem0 = (size_t(seg.b) * p.kv.max_seq * hkv + g) * D;
+    const bf16_t* kseg = static_cast<const bf16_t*>(p.kv.k) + elem0;
+    const bf16_t* vseg = static_cast<const bf16_t*>(p.kv.v) + elem0;
+
+    // Queries of this block in this lane's head order: slot h holds head h ^ gh(x), dims [8x, 8x+8).
+    u32x4_t q[GB];
+    {
+      const bf16_t* qrow = static_cast<const bf16_t*>(p.q) + (size_t(seg.b) * hq + g * group + hb * GB) * D;
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        const int head = h ^ ghx;
+        q[h] = hb * GB + head < group ? *reinterpret_cast<const u32x4_t*>(qrow + head * D + 8 * x)
+                                      : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+
+    float mh = -INFINITY;  // running max (log2 units) of head ghx
+    float lpart = 0.f;     // this lane's share of the sum of head ghx
+    float acc[GB][C::DL];
+#pragma unroll
+    for (int h = 0; h < GB; ++h)
+#pragma unroll
+      for (int i = 0; i < C::DL; ++i) acc[h][i] = 0.f;
+
+    auto rsrc_at = [&](const bf16_t* base, int j) {
+      const int key0 = j * kTileKeys;
+      const int left = (L - key0 - 1) * row_bytes + D * 2;  // valid bytes from the tile's first row
+      return __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<bf16_t*>(base) + size_t(key0) * hkv * D, (short)0, left > 0 ? left : 0, kRsrcWord3);
+    };
+    auto issue = [&](const bf16_t* base, int j, u32x4_t* buf) {
+      const __amdgpu_buffer_rsrc_t r = rsrc_at(base, j);
+#pragma unroll
+      for (int s = 0; s < C::NR; ++s) {
+        const int off = lane_off + (2 * (s >> 1) * C::RPI + (s & 1)) * row_bytes;
+        buf[s] = buffer_load16(r, off);
+      }
+    };
+
+    // Tile j: K in kb (two register stages, the next K tile always in flight),
+    // V in vb (one stage: the next V tile is issued as soon as this one is in LDS).
+    // k_next / v_next: tiles to issue into kb / vb once they are consumed (-1: none).
+    auto process = [&](int j, u32x4_t* kb, u32x4_t* vb, int k_next, int v_next) {
+      // ---- partial dots of slot s against the GB queries, then the head-splitting
+      // steps of the transpose-reduction (independent per slot, so each slot is
+      // reduced as soon as its dots are formed).
+      float R[C::NR][1];
+#pragma unroll
+      for (int s = 0; s < C::NR; ++s) {
+        float r8[GB];
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+          float a = dot2_bf16(q[h].x, kb[s].x, 0.f);
+          a = dot2_bf16(q[h].y, kb[s].y, a);
+          a = dot2_bf16(q[h].z, kb[s].z, a);
+          r8[h] = dot2_bf16(q[h].w, kb[s].w, a);
+        }
+#define KVC_HSTEP(K)                                                         \
+  if constexpr (K < C::HB) {                                                 \
+    constexpr int n = GB >> K;                                               \
+    _Pragma("unroll") for (int h = 0; h < n / 2; ++h)                        \
+      r8[h] += dpp<step_ctrl<LPR, K>()>(r8[h + n / 2]);                      \
+  }
+        KVC_HSTEP(0)
+        KVC_HSTEP(1)
+        KVC_HSTEP(2)
+#undef KVC_HSTEP
+        R[s][0] = r8[0];
+      }
+      if (k_next >= 0) issue(kseg, k_next, kb);  // this K stage is free again
+      // ---- row-splitting steps: the lane keeps the half of its slots its index bit selects
+      int off = 0;
+#define KVC_RSTEP(K)                                                         \
+  if constexpr (K >= C::HB && K < C::S) {                                    \
+    constexpr int nr = C::NR >> (K - C::HB);                                 \
+    const int bit = (x >> (C::S - 1 - K)) & 1;                               \
+    _Pragma("unroll") for (int r = 0; r < nr / 2; ++r) {                     \
+      const float keep = bit ? R[r + nr / 2][0] : R[r][0];                   \
+      const float send = bit ? R[r][0] : R[r + nr / 2][0];                   \
+      R[r][0] = keep + dpp<step_ctrl<LPR, K>()>(send);                       \
+    }                                                                        \
+    off += bit * (nr / 2);                                                   \
+  }
+      KVC_RSTEP(2)
+      KVC_RSTEP(3)
+#undef KVC_RSTEP
+      // ---- softmax of head ghx over this lane's NRK keys
+      const int key0 = j * kTileKeys;
+      float y[C::NRK];
+#pragma unroll
+      for (int r = 0; r < C::NRK; ++r) {
+        const int slot = r + off;
+        const int row = 2 * ((slot >> 1) * C::RPI + rg) + (slot & 1);
+        y[r] = key0 + row < L ? R[r][0] * c : -INFINITY;
+      }
+      bool raise = false;
+#pragma unroll
+      for (int r = 0; r < C::NRK; ++r) raise |= y[r] > mh + kLazyLog2;
+      if (__ballot(raise)) {
+        float ym = y[0];
+#pragma unroll
+        for (int r = 1; r < C::NRK; ++r) ym = fmaxf(ym, y[r]);
+        // lanes of one head: the row-splitting partners, then the other row groups
+        if constexpr (C::S - C::HB >= 1) ym = fmaxf(ym, __shfl_xor(ym, step_mask<LPR, C::S - 1>()));
+        if constexpr (C::S - C::HB >= 2) ym = fmaxf(ym, __shfl_xor(ym, step_mask<LPR, C::S - 2>()));
+#pragma unroll
+        for (int o = LPR; o < kWave; o <<= 1) ym = fmaxf(ym, __shfl_xor(ym, o));
+        const float m_new = fmaxf(mh, ym);  // finite: key 0 of the tile is always valid
+        const float alpha = exp2f(mh - m_new);
+        lpart *= alpha;
+        mh = m_new;
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+          const float ah = __shfl(alpha, lane_of_head<LPR, GB>(h));
+#pragma unroll
+          for (int i = 0; i < C::DL; ++i) acc[h][i] *= ah;
+        }
+      }
+      float pr[C::NRK];
+#pragma unroll
+      for (int r = 0; r < C::NRK; ++r) {
+        pr[r] = exp2f(y[r] - mh);
+        lpart += pr[r];
+      }
+      // ---- probabilities and V to this wave's LDS, both key-pair packed
+      wave_lds_fence();  // the previous tile's P*V reads are done
+#pragma unroll
+      for (int jp = 0; jp < C::NPK; ++jp) {
+        const int pair = ((2 * jp + off) >> 1) * C::RPI + rg;
+        plds[pair * GB + ghx] = pack_bf16x2(pr[2 * jp], pr[2 * jp + 1]);
+      }
+#pragma unroll
+      for (int sp = 0; sp < C::NR / 2; ++sp) {
+        const int pair = sp * C::RPI + rg;
+        const u32x4_t v0 = vb[2 * sp], v1 = vb[2 * sp + 1];
+        uint4 a, b;
+        a.x = pack_lo16(v0.x, v1.x); a.y = pack_hi16(v0.x, v1.x);
+        a.z = pack_lo16(v0.y, v1.y); a.w = pack_hi16(v0.y, v1.y);
+        b.x = pack_lo16(v0.z, v1.z); b.y = pack_hi16(v0.z, v1.z);
+        b.z = pack_lo16(v0.w, v1.w); b.w = pack_hi16(v0.w, v1.w);
+        uint4* dst = reinterpret_cast<uint4*>(vlds + (pair * D + 8 * x) * 4);
+        dst[0] = a;
+        dst[1] = b;
+      }
+      if (v_next >= 0) issue(vseg, v_next, vb);
+      wave_lds_fence();
+      // ---- P*V: lane owns dims [DL*lane, DL*lane + DL) of all GB heads
+#pragma unroll 4
+      for (int i = 0; i < C::NPAIR; ++i) {
+        uint32_t pw[GB];
+#pragma unroll
+        for (int h4 = 0; h4 < GB / 4; ++h4) {
+          const uint4 w4 = *reinterpret_cast<const uint4*>(plds + i * GB + 4 * h4);
+          pw[4 * h4] = w4.x; pw[4 * h4 + 1] = w4.y; pw[4 * h4 + 2] = w4.z; pw[4 * h4 + 3] = w4.w;
+        }
+        uint32_t vw[C::DL];
+        if constexpr (C::DL == 2) {
+          const uint2 v2 = *reinterpret_cast<const uint2*>(vlds + (i * D + 2 * lane) * 4);
+          vw[0] = v2.x;
+          vw[1] = v2.y;
+        } else {
+          vw[0] = *reinterpret_cast<const uint32_t*>(vlds + (i * D + lane) * 4);
+        }
+#pragma unroll
+        for (int h = 0; h < GB; ++h)
+#pragma unroll
+          for (int d = 0; d < C::DL; ++d) acc[h][d] = dot2_bf16(pw[h], vw[d], acc[h][d]);
+      }
+    };
+
+    // The wave's tiles of this run: j0 + wave, j0 + wave + 4, ...
+    u32x4_t kA[C::NR], kB[C::NR], vb[C::NR];
+    int j = j0 + wave;
+    if (j < j1) {
+      issue(kseg, j, kA);
+      issue(vseg, j, vb);
+      if (j + kWaves < j1) issue(kseg, j + kWaves, kB);
+    }
+    auto next = [&](int jj) { return jj < j1 ? jj : -1; };
+    while (j < j1) {
+      process(j, kA, vb, next(j + 2 * kWaves), next(j + kWaves));
+      j += kWaves;
+      if (j >= j1) break;
+      process(j, kB, vb, next(j + 2 * kWaves), next(j + kWaves));
+      j += kWaves;
+    }
+
+    // ---- fold the four waves' states of this run
+    // sum of head ghx over the lanes that hold it (row-splitting partners, then row groups)
+    if constexpr (C::S - C::HB >= 1) lpart += __shfl_xor(lpart, step_mask<LPR, C::S - 1>());
+    if constexpr (C::S - C::HB >= 2) lpart += __shfl_xor(lpart, step_mask<LPR, C::S - 2>());
+#pragma unroll
+    for (int o = LPR; o < kWave; o <<= 1) lpart += __shfl_xor(lpart, o);
+    __syncthreads();  // every wave is done with its V / P buffers
+    float* red_ml = reinterpret_cast<float*>(smem);            // [wave][GB][2]
+    float* red_o = red_ml + kWaves * GB * 2;                   // [wave][GB][D]
+    if (rg == 0) {  // lane lane_of_head(h) of row group 0 holds head h's max and sum
+#pragma unroll
+      for (int h = 0; h < GB; ++h)
+        if (x == lane_of_head<LPR, GB>(h)) {
+          red_ml[(wave * GB + h) * 2] = mh;
+          red_ml[(wave * GB + h) * 2 + 1] = lpart;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GB; ++h)
+#pragma unroll
+      for (int d = 0; d < C::DL; ++d) red_o[(wave * GB + h) * D + C::DL * lane + d] = acc[h][d];
+    __syncthreads();
+    const int slot = first_run ? 0 : 1;
+    for (int e = threadIdx.x; e < GB * D; e += kWaves * kWave) {
+      const int h = e / D;
+      const int d = e - h * D;
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, red_ml[(w * GB + h) * 2]);
+      float o = 0.f, l = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2f(red_ml[(w * GB + h) * 2] - mm);  // 0 for a wave with no tile here
+        o += f * red_o[(w * GB + h) * D + d];
+        l += f * red_ml[(w * GB + h) * 2 + 1];
+      }
+      if (complete) {
+        if (hb * GB + h < group)
+          static_cast<bf16_t*>(p.out)[(size_t(seg.b) * hq + g * group + hb * GB + h) * D + d] = f32_to_bf16(o / l);
+      } else {
+        const size_t ps = (size_t(blockIdx.x) * 2 + slot) * GB + h;
+        p.ws_o[ps * D + d] = o;
+        if (d == 0) {
+          p.ws_ml[ps * 2] = mm;
+          p.ws_ml[ps * 2 + 1] = l;
+        }
+      }
+    }
+    __syncthreads();  // LDS is reused by the next run
+
+    first_run = false;
+    t = run_end;
+    if (t < t_end) {  // next segment (rows of length 0 hold no tiles and are skipped)
+      seg.base = seg_end;
+      if (++seg.sr == spr) {
+        seg.sr = 0;
+        do {
+          ++seg.b;
+          seg.nt = row_tiles(p.kv.seqlens, seg.b, p.kv.max_seq);
+        } while (seg.nt == 0);
+      }
+    }
+  }
+}
+
+// Fold the partials of one (segment, query head): one workgroup each.
+template <int D, int GB>
+__global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p) {
+  constexpr int kChunks = D / 4;          // 16-byte chunks of an o row
+  constexpr int kPI = 256 / kChunks;      // partials processed side by side
+  __shared__ float red[kPI][D];
+  __shared__ float red_l[kPI];
+  __shared__ float red_m[4];
+
+  const int spr = p.kv.n_kv_heads * p.n_hb;
+  const int h = blockIdx.x % GB;
+  const int seg = blockIdx.x / GB;
+  const int b = seg / spr;
+  const int sr = seg - b * spr;
+  const int g = sr / p.n_hb;
+  const int hb = sr - g * p.n_hb;
+  const int hq = p.n_q_heads;
+  const int group = hq / p.kv.n_kv_heads;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+
+  const int nt = row_tiles(p.kv.seqlens, b, p.kv.max_seq);
+  if (nt == 0) {
+    if (sr == 0 && h == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
+    return;
+  }
+  if (hb * GB + h >= group) return;  // padding head of the last block
+  // N and this segment's first tile
+  int n_all = 0, before = 0;
+  for (int b0 = 0; b0 < p.kv.batch; b0 += kWave) {
+    const int bb = b0 + lane;
+    const int v = bb < p.kv.batch ? row_tiles(p.kv.seqlens, bb, p.kv.max_seq) : 0;
+    n_all += wave_sum_i(v);
+    before += wave_sum_i(bb < b ? v : 0);
+  }
+  const int n_tiles = n_all * spr;
+  const int base = before * spr + sr * nt;
+  // workgroup holding tile t: the largest w with w N / P <= t
+  auto wg_of = [&](int t) { return int(((long long)(t + 1) * p.n_wg - 1) / n_tiles); };
+  const int w_first = wg_of(base);
+  const int w_last = wg_of(base + nt - 1);
+  if (w_first == w_last) return;  // written directly by the split pass
+  // Partials: w_first's run here (its first run -- slot 0 -- if its range starts at this
+  // segment, else its last -- slot 1), then the first run (slot 0) of every later
+  // workgroup up to w_last.  Workgroups with an empty range (fewer tiles than
+  // workgroups) wrote nothing and are skipped.
+  const int count = w_last - w_first + 1;
+  const int slot0 = range_begin(w_first, n_tiles, p.n_wg) == base ? 0 : 1;
+  auto part = [&](int i) { return (size_t(w_first + i) * 2 + (i == 0 ? slot0 : 0)) * GB + h; };
+  auto empty = [&](int i) {
+    return range_begin(w_first + i, n_tiles, p.n_wg) == range_begin(w_first + i + 1LL, n_tiles, p.n_wg);
+  };
+
+  float mx = -INFINITY;
+  for (int i = threadIdx.x; i < count; i += blockDim.x)
+    if (!empty(i)) mx = fmaxf(mx, p.ws_ml[part(i) * 2]);
+  mx = wave_max(mx);
+  if (lane == 0) red_m[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+
+  const int ck = threadIdx.x % kChunks;
+  const int pi = threadIdx.x / kChunks;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  for (int i = pi; i < count; i += kPI) {
+    if (empty(i)) continue;
+    const size_t ps = part(i);
+    const float f = exp2f(p.ws_ml[ps * 2] - M);
+    const float4 o = *reinterpret_cast<const float4*>(p.ws_o + ps * D + 4 * ck);
+    a.x += f * o.x; a.y += f * o.y; a.z += f * o.z; a.w += f * o.w;
+    den += f * p.ws_ml[ps * 2 + 1];
+  }
+  *reinterpret_cast<float4*>(&red[pi][4 * ck]) = a;
+  if (ck == 0) red_l[pi] = den;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPI; ++k) {
+      o += red[k][threadIdx.x];
+      l += red_l[k];
+    }
+    static_cast<bf16_t*>(p.out)[(size_t(b) * hq + g * group + hb * GB + h) * D + threadIdx.x] = f32_to_bf16(o / l);
+  }
+}
+
+template <int D, int GB>
+hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((decode_bf16_kernel<D, GB>), dim3(p.n_wg), dim3(kWaves * kWave), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long n_comb = (long long)p.kv.batch * p.kv.n_kv_heads * p.n_hb * GB;
+  hipLaunchKernelGGL((decode_bf16_combine_kernel<D, GB>), dim3(unsigned(n_comb)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D, int GB>
+int occupancy_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(decode_bf16_kernel<D, GB>),
+                                                   kWaves * kWave, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+}  // namespace
+
+int decode_bf16_block(int group) { return group <= 4 ? 4 : 8; }
+
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t s) {
+  if (p.kv.head_dim == 128) return p.gb == 4 ? launch_t<128, 4>(p, s) : launch_t<128, 8>(p, s);
+  return p.gb == 4 ? launch_t<64, 4>(p, s) : launch_t<64, 8>(p, s);
+}
+
+int decode_bf16_occupancy(int head_dim, int gb) {
+  if (head_dim == 128) return gb == 4 ? occupancy_t<128, 4>() : occupancy_t<128, 8>();
+  return gb == 4 ? occupancy_t<64, 4>() : occupancy_t<64, 8>();
+}
+
+}  // namespace kvc

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kvc.h"
 #include "kvc_launch.h"
 
@@ -47,11 +49,47 @@ bool resolve_scale(float scale, int32_t head_dim, float* out) {
   return true;
 }
 
-int32_t resolve_split(int32_t split_keys) { return split_keys == 0 ? kDefaultSplitKeys : split_keys; }
+// Workgroups the bfloat16 decode spreads its tiles over: every CU times the
+// workgroups one CU holds at once.  Read-only device properties, cached per
+// device on first use.
+int32_t default_decode_workers(int32_t head_dim, int32_t gb) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int32_t> cache[kMaxDev][4];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  const int variant = (head_dim == 128 ? 2 : 0) + (gb == 8 ? 1 : 0);
+  if (dev < kMaxDev) {
+    const int32_t v = cache[dev][variant].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  const int occ = kvc::decode_bf16_occupancy(head_dim, gb);
+  const int32_t n = cus * (occ > 0 ? occ : 1);
+  if (dev < kMaxDev) cache[dev][variant].store(n, std::memory_order_relaxed);
+  return n;
+}
 
-size_t decode_ws_bytes(const kvc_cache* c, int32_t n_q_heads, int32_t split_keys) {
-  const int32_t sk = resolve_split(split_keys);
-  const int64_t max_splits = (int64_t(c->max_seq) + sk - 1) / sk;
+struct DecodePlan {
+  int32_t gb, n_hb, n_wg;
+};
+
+DecodePlan decode_plan(const kvc_cache* c, int32_t n_q_heads, int32_t n_workers) {
+  DecodePlan pl;
+  const int32_t group = n_q_heads / c->n_kv_heads;
+  pl.gb = kvc::decode_bf16_block(group);
+  pl.n_hb = (group + pl.gb - 1) / pl.gb;
+  pl.n_wg = n_workers > 0 ? n_workers : default_decode_workers(c->head_dim, pl.gb);
+  return pl;
+}
+
+size_t decode_ws_bytes(const kvc_cache* c, int32_t n_q_heads, int32_t n_workers) {
+  if (c->dtype == KVC_BF16) {
+    const DecodePlan pl = decode_plan(c, n_q_heads, n_workers);
+    if (pl.n_wg <= 0) return 0;
+    return size_t(pl.n_wg) * 2 * size_t(pl.gb) * size_t(c->head_dim + 2) * sizeof(float);
+  }
+  const int64_t max_splits = (int64_t(c->max_seq) + kDefaultSplitKeys - 1) / kDefaultSplitKeys;
   if (max_splits <= 1) return 0;  // every row fits one split: written directly
   return size_t(c->batch) * size_t(n_q_heads) * size_t(max_splits) * size_t(c->head_dim + 2) * sizeof(float);
 }
@@ -88,40 +126,63 @@ int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* 
   return launch_status(kvc::launch_rope_append(p, static_cast<hipStream_t>(stream)));
 }
 
-size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int32_t split_keys) {
+size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int32_t n_workers) {
   if (check_cache(cache) != KVC_OK || check_heads(cache, n_q_heads) != KVC_OK) return 0;
-  if (split_keys < 0 || split_keys % 64 != 0) return 0;
-  return decode_ws_bytes(cache, n_q_heads, split_keys);
+  if (n_workers < 0) return 0;
+  return decode_ws_bytes(cache, n_q_heads, n_workers);
 }
 
 int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out, int32_t n_q_heads,
-                    float scale, int32_t split_keys, void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                    float scale, int32_t n_workers, void* workspace, size_t workspace_bytes, int32_t* dev_err,
                     void* stream) {
   int st = check_cache(cache);
   if (st != KVC_OK) return st;
   if (layer < 0 || layer >= cache->n_layers) return KVC_E_ARG;
   if (!q_rot || !out || !aligned16(q_rot) || !aligned16(out)) return KVC_E_ARG;
   if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
-  if (split_keys < 0 || split_keys % 64 != 0) return KVC_E_ARG;
-  kvc::SplitParams p;
-  if (!resolve_scale(scale, cache->head_dim, &p.scale_log2)) return KVC_E_ARG;
-  p.scale_log2 *= 1.4426950408889634f;
-  const int32_t sk = resolve_split(split_keys);
-  const size_t need = decode_ws_bytes(cache, n_q_heads, split_keys);
+  if (n_workers < 0) return KVC_E_ARG;
+  float sc;
+  if (!resolve_scale(scale, cache->head_dim, &sc)) return KVC_E_ARG;
+  const size_t need = decode_ws_bytes(cache, n_q_heads, n_workers);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return KVC_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->dtype == KVC_BF16) {
+    const DecodePlan pl = decode_plan(cache, n_q_heads, n_workers);
+    if (pl.n_wg <= 0) return KVC_E_LAUNCH;
+    // Flattened tile indices and in-row byte offsets are 32-bit.
+    const int64_t tiles = int64_t(cache->batch) * cache->n_kv_heads * pl.n_hb * ((int64_t(cache->max_seq) + 31) / 32);
+    const int64_t row_span = int64_t(cache->max_seq) * cache->n_kv_heads * cache->head_dim * 2;
+    if (tiles >= (int64_t(1) << 31) || row_span >= (int64_t(1) << 31)) return KVC_E_SHAPE;
+    if (int64_t(cache->batch) * cache->n_kv_heads * pl.n_hb * pl.gb > 0x7fffffffLL) return KVC_E_SHAPE;
+    kvc::DecodeParams p;
+    p.kv = layer_view(cache, layer);
+    p.q = q_rot;
+    p.out = out;
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_ml = p.ws_o + size_t(pl.n_wg) * 2 * pl.gb * cache->head_dim;
+    p.n_q_heads = n_q_heads;
+    p.n_wg = pl.n_wg;
+    p.gb = pl.gb;
+    p.n_hb = pl.n_hb;
+    p.scale_log2 = sc * 1.4426950408889634f;
+    p.dev_err = dev_err;
+    return launch_status(kvc::launch_decode_bf16(p, s));
+  }
+  // float32: split-KV over fixed 512-key splits.
+  kvc::SplitParams p;
+  p.scale_log2 = sc * 1.4426950408889634f;
   p.kv = layer_view(cache, layer);
   p.q = q_rot;
   p.out = out;
   p.T = 1;
   p.n_q_heads = n_q_heads;
-  p.split_keys = sk;
-  p.max_splits = int32_t((int64_t(cache->max_seq) + sk - 1) / sk);
+  p.split_keys = kDefaultSplitKeys;
+  p.max_splits = int32_t((int64_t(cache->max_seq) + kDefaultSplitKeys - 1) / kDefaultSplitKeys);
   p.direct = need == 0;
   p.ws_o = static_cast<float*>(workspace);
   p.ws_ml = p.direct ? nullptr
                      : p.ws_o + size_t(cache->batch) * n_q_heads * size_t(p.max_splits) * cache->head_dim;
   p.dev_err = dev_err;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = kvc::launch_split_attention(p, s);
   if (e == hipSuccess && !p.direct) e = kvc::launch_split_combine(p, s);
   return launch_status(e);

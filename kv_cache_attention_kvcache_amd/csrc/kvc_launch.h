@@ -47,6 +47,23 @@ struct SplitParams {
 hipError_t launch_split_attention(const SplitParams& p, hipStream_t s);
 hipError_t launch_split_combine(const SplitParams& p, hipStream_t s);
 
+// bfloat16 decode (T = 1): persistent split-KV over a balanced tile partition.
+// A segment is (row, KV head, block of gb query heads); workgroup w of n_wg
+// takes the flattened tiles [w N / n_wg, (w+1) N / n_wg).
+struct DecodeParams {
+  LayerView kv;
+  const void* q;
+  void* out;
+  float* ws_o;   // (n_wg, 2, gb, head_dim): unnormalised partial outputs
+  float* ws_ml;  // (n_wg, 2, gb, 2): running max (log2 units) and sum
+  int32_t n_q_heads, n_wg, gb, n_hb;
+  float scale_log2;
+  int32_t* dev_err;
+};
+int decode_bf16_block(int group);                  // query heads per block (4 or 8)
+int decode_bf16_occupancy(int head_dim, int gb);   // resident workgroups per CU
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t s);
+
 struct PrefillParams {
   LayerView kv;
   const void* q;

@@ -62,13 +62,19 @@ def test_status_strings(lib):
 
 
 def test_workspace_query_is_a_host_function(lib):
+    W = lib.lib.kvc_decode_workspace_bytes
     d = _desc(lib, max_seq=4096, batch=8, head_dim=128)
-    n = lib.lib.kvc_decode_workspace_bytes(ctypes.byref(d), 16, 0)
-    assert n == 8 * 16 * 8 * (128 + 2) * 4  # 4096 / 512 = 8 splits of 512 keys
-    assert lib.lib.kvc_decode_workspace_bytes(ctypes.byref(d), 16, 64) == 8 * 16 * 64 * 130 * 4
-    assert lib.lib.kvc_decode_workspace_bytes(ctypes.byref(_desc(lib, max_seq=512)), 16, 0) == 0  # one split
-    assert lib.lib.kvc_decode_workspace_bytes(ctypes.byref(d), 6, 0) == 0  # 6 % 4 != 0: invalid
-    assert lib.lib.kvc_decode_workspace_bytes(ctypes.byref(d), 16, 100) == 0  # not a multiple of 64
+    # bfloat16: two partial slots per workgroup, each (max, sum, o) for a block of 4 (group <= 4) or 8 heads
+    assert W(ctypes.byref(d), 16, 64) == 64 * 2 * 4 * (128 + 2) * 4
+    assert W(ctypes.byref(d), 32, 64) == 64 * 2 * 8 * (128 + 2) * 4
+    assert W(ctypes.byref(_desc(lib, head_dim=64)), 64, 10) == 10 * 2 * 8 * (64 + 2) * 4
+    # float32: fixed 512-key splits per (row, query head); the worker count is ignored
+    f = _desc(lib, max_seq=4096, batch=8, dtype=lib.KVC_F32)
+    assert W(ctypes.byref(f), 16, 0) == 8 * 16 * 8 * (128 + 2) * 4
+    assert W(ctypes.byref(f), 16, 7) == 8 * 16 * 8 * (128 + 2) * 4
+    assert W(ctypes.byref(_desc(lib, max_seq=512, dtype=lib.KVC_F32)), 16, 0) == 0  # one split: none needed
+    assert W(ctypes.byref(d), 6, 4) == 0  # 6 % 4 != 0: invalid
+    assert W(ctypes.byref(d), 16, -1) == 0  # negative worker count: invalid
 
 
 def test_rope_append_validation(lib):
@@ -99,8 +105,10 @@ def test_decode_and_prefill_validation(lib):
     L = lib.lib
     d = _desc(lib, max_seq=4096)
     q = P(0x40000)
-    assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 16, 0.0, 0, None, 0, None, None) == lib.KVC_E_WORKSPACE
-    assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 16, 0.0, 100, None, 0, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 16, 0.0, 8, None, 0, None, None) == lib.KVC_E_WORKSPACE
+    assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 16, 0.0, 8, P(0x70000), 8 * 2 * 4 * 130 * 4 - 4, None,
+                             None) == lib.KVC_E_WORKSPACE  # one float short
+    assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 16, 0.0, -1, None, 0, None, None) == lib.KVC_E_ARG
     assert L.kvc_attn_decode(ctypes.byref(d), 0, q, q, 16, float("nan"), 0, P(0x70000), 1 << 30, None,
                              None) == lib.KVC_E_ARG
     assert L.kvc_attn_decode(ctypes.byref(d), 5, q, q, 16, 0.0, 0, P(0x70000), 1 << 30, None, None) == lib.KVC_E_ARG

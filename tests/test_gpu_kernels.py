@@ -186,7 +186,7 @@ def test_clone_errors(kvc):
 DECODE_LENGTHS = [0, 1, 63, 64, 65, 700, 1500, 4095]
 
 
-def _decode_case(kvc, dtype, hq, hkv, d, lengths, split_keys, spike=False, seed=0):
+def _decode_case(kvc, dtype, hq, hkv, d, lengths, n_workers, spike=False, seed=0):
     g = _rng(5, hq, d, seed)
     batch, max_seq = len(lengths), max(lengths) + 1
     cache = make_cache(kvc, 2, batch, max_seq, hkv, d, dtype)
@@ -197,18 +197,19 @@ def _decode_case(kvc, dtype, hq, hkv, d, lengths, split_keys, spike=False, seed=
     if spike:  # the new key of group 0 parallel to its first query: that row's output ~ its value
         k[:, 0, 0] = 12.0 * np.sqrt(d) * q[:, 0, 0] / np.sum(q[:, 0, 0] ** 2, axis=-1, keepdims=True)
     q_rot = kvc.kvc_rope_append(cache, 1, dev(q, dtype), dev(k, dtype), dev(v, dtype))
-    out = kvc.kvc_attn_decode(cache, 1, q_rot, split_keys=split_keys)
+    out = kvc.kvc_attn_decode(cache, 1, q_rot, n_workers=n_workers)
     torch.cuda.synchronize()
     ref = np.stack([oatt.decode_over_existing(hist_k[b], hist_v[b], q[b, 0], k[b, 0], v[b, 0], dtype)
                     for b in range(batch)])
     return host64(out)[:, 0], ref, (hist_k, hist_v, q, k, v)
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,d", SHAPES)
-@pytest.mark.parametrize("split_keys", [0, 64, 192])
-def test_decode_matches_oracle(kvc, dtype, hq, hkv, d, split_keys):
-    out, ref, _ = _decode_case(kvc, dtype, hq, hkv, d, DECODE_LENGTHS, split_keys)
-    gates.check(out, ref, dtype, f"decode {dtype} {hq}/{hkv} D{d} split {split_keys}")
+@pytest.mark.parametrize("dtype,hq,hkv,d", SHAPES + [("bf16", 32, 2, 128), ("bf16", 6, 2, 128)])
+@pytest.mark.parametrize("n_workers", [0, 1, 7, 300])
+def test_decode_matches_oracle(kvc, dtype, hq, hkv, d, n_workers):
+    """Ragged lengths (1 to 4096 keys) over every head layout: GQA groups 1, 3, 4, 8 and 16."""
+    out, ref, _ = _decode_case(kvc, dtype, hq, hkv, d, DECODE_LENGTHS, n_workers)
+    gates.check(out, ref, dtype, f"decode {dtype} {hq}/{hkv} D{d} workers {n_workers}")
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 64, 8, 128), ("f32", 4, 4, 64)])
@@ -251,16 +252,35 @@ def test_decode_spike_rows_and_mutants_fail(kvc, dtype, hq, hkv, d):
 
 
 def test_decode_split_count_independence_and_determinism(kvc):
+    """The split-KV partition changes only the float32 addition order (one worker = no split at all)."""
     dtype, hq, hkv, d = "bf16", 64, 8, 128
     outs = {}
-    for sk in (64, 128, 448, 4096):
-        out, ref, _ = _decode_case(kvc, dtype, hq, hkv, d, [1, 777, 3000, 4095], sk, seed=3)
-        gates.check(out, ref, dtype, f"split {sk}")
-        outs[sk] = out
-    for sk in (64, 128, 448):
-        gates.check(outs[sk], outs[4096], dtype, f"split {sk} vs one split")
-    again, _, _ = _decode_case(kvc, dtype, hq, hkv, d, [1, 777, 3000, 4095], 128, seed=3)
-    assert np.array_equal(again, outs[128])  # run-to-run bit-identical
+    for nw in (1, 3, 64, 1000, 0):
+        out, ref, _ = _decode_case(kvc, dtype, hq, hkv, d, [1, 777, 3000, 4095], nw, seed=3)
+        gates.check(out, ref, dtype, f"workers {nw}")
+        outs[nw] = out
+    for nw in (3, 64, 1000, 0):
+        gates.check(outs[nw], outs[1], dtype, f"workers {nw} vs one worker")
+    again, _, _ = _decode_case(kvc, dtype, hq, hkv, d, [1, 777, 3000, 4095], 64, seed=3)
+    assert np.array_equal(again, outs[64])  # run-to-run bit-identical
+
+
+def test_decode_batch_row_equals_single_row_run(kvc):
+    """Row b of a batch decodes like a batch-1 cache holding only row b (nanochat's clone-then-diverge flow)."""
+    dtype, hq, hkv, d = "bf16", 16, 4, 128
+    lengths = [2000, 5, 2047, 1200]
+    out, ref, (hk, hv, q, k, v) = _decode_case(kvc, dtype, hq, hkv, d, lengths, 0, seed=4)
+    for b in range(len(lengths)):
+        one = make_cache(kvc, 1, 1, max(lengths) + 1, hkv, d, dtype)
+        n = lengths[b]
+        one.k[0, 0, :n] = dev(hk[b], dtype)
+        one.v[0, 0, :n] = dev(hv[b], dtype)
+        one.seqlens.fill_(n)
+        q_rot = kvc.kvc_rope_append(one, 0, dev(q[b:b + 1], dtype), dev(k[b:b + 1], dtype), dev(v[b:b + 1], dtype))
+        single = host64(kvc.kvc_attn_decode(one, 0, q_rot))[0, 0]
+        torch.cuda.synchronize()
+        gates.check(out[b], single, dtype, f"row {b} in batch vs alone")
+        gates.check(single, ref[b], dtype, f"row {b} alone vs oracle")
 
 
 def test_decode_capacity_and_workspace_errors(kvc):
