@@ -4,8 +4,8 @@
  * A C ABI over four operations and two helpers.  Every pointer named
  * "device" must point to memory on the current HIP device; the library never
  * allocates, never frees and keeps no pointer after a call returns.  Its only
- * state is a per-device cache of read-only device properties (CU count,
- * kernel occupancy), so calls on different streams are independent.
+ * state is a per-device cache of a read-only device property (the CU count),
+ * so calls on different streams are independent.
  * Every call is asynchronous on the given stream (a hipStream_t passed as
  * void*, NULL for the default stream) and never synchronises the device.
  *
@@ -126,8 +126,8 @@ size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int
  *   out    device, same shape as q_rot.
  *   scale  softmax scale; <= 0 selects 1/sqrt(head_dim).
  *   n_workers  bfloat16 caches: the number of workgroups the cached keys of
- *          all rows are split evenly over (split-KV); 0 = as many as the
- *          device runs at once.  Float32 caches use fixed 512-key splits and
+ *          all rows are split evenly over (split-KV); 0 = one per compute
+ *          unit of the current device.  Float32 caches use fixed 512-key splits and
  *          ignore it.  A result depends on the lengths of all rows and on
  *          n_workers only through the order of float32 additions; it is
  *          bit-identical run to run for the same inputs and n_workers.

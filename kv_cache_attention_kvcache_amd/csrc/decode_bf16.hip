@@ -8,8 +8,8 @@
 //
 // Work partition.  A segment is (row b, KV head g, block hb of GB query heads
 // of its group); it holds ceil(L_b / 32) tiles of 32 keys, L_b = seqlens[b]+1.
-// All segments laid end to end form N tiles; the grid is persistent (as many
-// workgroups as the device holds at once) and workgroup w takes the tiles
+// All segments laid end to end form N tiles; the grid is persistent (one
+// workgroup per CU by default) and workgroup w takes the tiles
 // [w N / P, (w+1) N / P) -- the same K/V bytes per workgroup whatever the
 // lengths, so batch 1 at 73K keys and batch 64 with ragged lengths balance
 // alike.  The range is cut into runs (its intersection with each segment);
@@ -119,8 +119,12 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), K, 0xf, 0xf, true));
 }
 
+// 16-byte buffer load with the non-temporal hint: K/V are streamed once per
+// call, and keeping them out of the caches' retention lifts the sustained read
+// rate (measured on MI355X: about 5.6 -> 6.6 TB/s for 256-byte rows at a 2 KiB stride).
+constexpr int kCpolNT = 2;
 __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, kCpolNT);
 }
 
 // Number of 32-key tiles of row b, or 0 if its length is out of range.
@@ -191,7 +195,7 @@ __device__ SegPos find_segment(const DecodeParams& p, int t, int lane) {
 __device__ __forceinline__ int range_begin(long long w, int n, int n_wg) { return int(w * n / n_wg); }
 
 template <int D, int GB>
-__global__ __launch_bounds__(kWaves * kWave, 2) void decode_bf16_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodeParams p) {
   using C = Cfg<D, GB>;
   constexpr int LPR = C::LPR;
   __shared__ __align__(16) uint8_t smem[C::kLds];
@@ -582,15 +586,6 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int GB>
-int occupancy_t() {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(decode_bf16_kernel<D, GB>),
-                                                   kWaves * kWave, 0) != hipSuccess)
-    return 0;
-  return n;
-}
-
 }  // namespace
 
 int decode_bf16_block(int group) { return group <= 4 ? 4 : 8; }
@@ -598,11 +593,6 @@ int decode_bf16_block(int group) { return group <= 4 ? 4 : 8; }
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t s) {
   if (p.kv.head_dim == 128) return p.gb == 4 ? launch_t<128, 4>(p, s) : launch_t<128, 8>(p, s);
   return p.gb == 4 ? launch_t<64, 4>(p, s) : launch_t<64, 8>(p, s);
-}
-
-int decode_bf16_occupancy(int head_dim, int gb) {
-  if (head_dim == 128) return gb == 4 ? occupancy_t<128, 4>() : occupancy_t<128, 8>();
-  return gb == 4 ? occupancy_t<64, 4>() : occupancy_t<64, 8>();
 }
 
 }  // namespace kvc

@@ -61,7 +61,6 @@ struct DecodeParams {
   int32_t* dev_err;
 };
 int decode_bf16_block(int group);                  // query heads per block (4 or 8)
-int decode_bf16_occupancy(int head_dim, int gb);   // resident workgroups per CU
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t s);
 
 struct PrefillParams {
