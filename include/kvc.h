@@ -159,7 +159,9 @@ int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, vo
  *   out    device, same shape.
  *   scale  softmax scale; <= 0 selects 1/sqrt(head_dim).
  *
- * Rows with P < 0 or P + T > max_seq are skipped (KVC_DEV_CAPACITY).
+ * Rows with P < 0 or P + T > max_seq are skipped (KVC_DEV_CAPACITY).  bfloat16
+ * caches whose one head row (max_seq * n_kv_heads * head_dim elements) reaches
+ * 2^30 are rejected with KVC_E_SHAPE.
  */
 int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out,
                      int32_t T, int32_t n_q_heads, float scale, int32_t* dev_err, void* stream);

@@ -198,6 +198,8 @@ int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, v
   if (!resolve_scale(scale, cache->head_dim, &sc)) return KVC_E_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->dtype == KVC_BF16) {
+    // The kernel's buffer descriptors span one head row with 32-bit byte offsets.
+    if (int64_t(cache->max_seq) * cache->n_kv_heads * cache->head_dim * 2 >= (int64_t(1) << 31)) return KVC_E_SHAPE;
     kvc::PrefillParams p;
     p.kv = layer_view(cache, layer);
     p.q = q_rot;

@@ -26,9 +26,12 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(bf16_t, h);
 }
 
-// Two floats -> packed bfloat16 pair (lo = a, hi = b), round to nearest even.
+// Two floats -> packed bfloat16 pair (lo = a, hi = b), round to nearest even
+// (one v_cvt_pk_bf16_f32).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // acc + a.lo*b.lo + a.hi*b.hi on packed bfloat16 pairs (v_dot2_f32_bf16, float32 accumulate).

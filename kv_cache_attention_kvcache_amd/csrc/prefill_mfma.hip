@@ -36,6 +36,13 @@ namespace {
 constexpr int kBM = 128;  // queries per workgroup
 constexpr int kBN = 64;   // keys per tile
 constexpr int kWQ = 32;   // queries per wave
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data format (gfx9 family)
+constexpr float kLazyLog2 = 8.f;  // probabilities may reach 2^8 before the running max is raised
+constexpr uint32_t kBf16One2 = 0x3F803F80u;  // (1.0, 1.0) as a bfloat16 pair
+
+// 2^x on the transcendental unit, without the denormal-result fix-up of exp2f:
+// softmax weights below 2^-126 flush to zero, which the float32 sums cannot see.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -107,27 +114,31 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
 
   // Staging roles.  K: thread loads 16-byte chunks f = tid + 256 i of the tile.
   // V: thread owns keys 4 kq .. 4 kq + 3 and head dims 8 dc .. 8 dc + 7.
+  // Loads are range-checked buffer loads whose descriptor starts at the tile's
+  // first key: keys at or past kend_wg read as zeros, with no branch.
   const int kq = tid & 15;
   const int dc = tid >> 4;
   const bool v_active = dc < D / 8;
+  const int row_bytes = hkv * D * 2;
+  const int k_off = (tid / (D / 8)) * row_bytes + (tid % (D / 8)) * 16;  // + i * (256 / (D/8)) rows
+  const int v_off = 4 * kq * row_bytes + dc * 16;                         // + r rows
   uint4 kreg[kKLoads], vreg[4];
+  auto tile_rsrc = [&](const bf16_t* base, int kb0) {
+    const int left = (kend_wg - kb0 - 1) * row_bytes + D * 2;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base) + size_t(kb0) * key_stride, (short)0,
+                                             left > 0 ? left : 0, kRsrcWord3);
+  };
   auto load_tile = [&](int kb0) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k_base, kb0);
 #pragma unroll
-    for (int i = 0; i < kKLoads; ++i) {
-      const int f = tid + 256 * i;
-      const int r = f / (D / 8);
-      const int c = f % (D / 8);
-      const int key = kb0 + r;
-      kreg[i] = key < kend_wg ? *reinterpret_cast<const uint4*>(k_base + key * key_stride + c * 8)
-                              : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < kKLoads; ++i)
+      kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rk, k_off + i * (256 / (D / 8)) * row_bytes, 0, 0));
     if (v_active) {
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v_base, kb0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb0 + 4 * kq + r;
-        vreg[r] = key < kend_wg ? *reinterpret_cast<const uint4*>(v_base + key * key_stride + dc * 8)
-                                : make_uint4(0, 0, 0, 0);
-      }
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + r * row_bytes, 0, 0));
     }
   };
   auto store_tile = [&]() {
@@ -170,18 +181,17 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
     if (it + 1 < n_tiles) load_tile(kb0 + kBN);
     if (kb0 >= kend_w) continue;  // nothing visible to this wave here
 
-    // ---- S^T for 2 blocks of 32 keys
+    // ---- S^T for 2 blocks of 32 keys (the first k-step starts from a zero accumulator)
     f32x16_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
       const uint8_t* arow_p = k_lds + (32 * kb + arow) * kKStride + 16 * half;
 #pragma unroll
       for (int kd = 0; kd < kKD; ++kd) {
         const uint4 a = *reinterpret_cast<const uint4*>(arow_p + 32 * kd);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                        __builtin_bit_cast(bf16x8_t, qf[kd]), s[kb], 0, 0, 0);
+                                                        __builtin_bit_cast(bf16x8_t, qf[kd]),
+                                                        kd == 0 ? f32x16_t{} : s[kb], 0, 0, 0);
       }
     }
     // Score register r of block kb belongs to key kb0 + 32 kb + 8 half + (r & 7) + 16 (r >> 3).
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb0 + 32 * kb + 8 * half + (r & 7) + 16 * (r >> 3);
-          if (key > my_pos) s[kb][r] = -INFINITY;
+          s[kb][r] = key > my_pos ? -INFINITY : s[kb][r];
         }
     }
     float mx = -INFINITY;
@@ -199,11 +209,20 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx * c);  // finite: key 0 is visible to every query
-    const float alpha = exp2f(m - m_new);
-    m = m_new;
-    float rowsum = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // this query's tile max, log2 units (finite: key 0 is visible)
+    // Lazy maximum: m is raised (and o, l rescaled) only when a score exceeds it
+    // by more than 2^8; otherwise probabilities up to 2^8 are accumulated as they
+    // are.  The decision is wave-uniform.
+    if (__ballot(mx > m + kLazyLog2)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);  // 0 on the first visible tile (m = -inf)
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
     uint4 pf[4];  // B operands of the 4 k-steps of 16 keys
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -212,19 +231,14 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = exp2f(fmaf(s[kb][8 * hh + 2 * j], c, -m_new));
-          const float p1 = exp2f(fmaf(s[kb][8 * hh + 2 * j + 1], c, -m_new));
-          rowsum += p0 + p1;
+          const float p0 = fast_exp2(fmaf(s[kb][8 * hh + 2 * j], c, -m));
+          const float p1 = fast_exp2(fmaf(s[kb][8 * hh + 2 * j + 1], c, -m));
           w[j] = pack_bf16x2(p0, p1);
+          l = dot2_bf16(w[j], kBf16One2, l);  // the sum of the rounded probabilities P*V uses
         }
         pf[2 * kb + hh] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
-    l = l * alpha + rowsum;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
