@@ -7,7 +7,7 @@
 // P = seqlens[b], sees keys 0 .. P + t.
 //
 // This is the dense contraction of the path, so it runs on matrix cores.
-// One workgroup = 128 queries of one query head (4 waves x 32 queries),
+// One workgroup = 256 queries of one query head (8 waves x 32 queries),
 // looping over 64-key tiles of its KV head:
 //   * S^T = K Q^T on MFMA: the K tile is the A operand from LDS (padded rows,
 //     conflict-free), the wave's 32 query rows are the B operand held in
@@ -33,7 +33,8 @@ namespace kvc {
 
 namespace {
 
-constexpr int kBM = 128;  // queries per workgroup
+constexpr int kThreads = 512;  // 8 waves per workgroup
+constexpr int kBM = 256;  // queries per workgroup (8 waves x 32)
 constexpr int kBN = 64;   // keys per tile
 constexpr int kWQ = 32;   // queries per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data format (gfx9 family)
@@ -56,14 +57,14 @@ __device__ __forceinline__ int perm_row(int i) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams p) {
   constexpr int kKStride = D * 2 + 16;        // bytes per K row in LDS
   constexpr int kVStride = kBN * 2 + 16;      // bytes per transposed V row (one head dim)
   constexpr int kKD = D / 16;                 // MFMA k-steps over the head dim
   constexpr int kDB = D / 32;                 // 32-dim output blocks
-  constexpr int kKLoads = kBN * D * 2 / 16 / 256;  // 16-byte K loads per thread per tile
-  __shared__ __align__(16) uint8_t k_lds[kBN * kKStride];
-  __shared__ __align__(16) uint8_t v_lds[D * kVStride];
+  constexpr int kKLoads = kBN * D * 2 / 16 / kThreads;  // 16-byte K loads per thread per tile
+  __shared__ __align__(16) uint8_t k_lds[2][kBN * kKStride];  // K tiles, two buffers
+  __shared__ __align__(16) uint8_t v_lds[2][D * kVStride];    // V^T tiles, two buffers
 
   const int hq = p.n_q_heads;
   const int hkv = p.kv.n_kv_heads;
@@ -112,53 +113,54 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
   const bf16_t* k_base = static_cast<const bf16_t*>(p.kv.k) + size_t(b) * p.kv.max_seq * key_stride + size_t(g) * D;
   const bf16_t* v_base = static_cast<const bf16_t*>(p.kv.v) + size_t(b) * p.kv.max_seq * key_stride + size_t(g) * D;
 
-  // Staging roles.  K: thread loads 16-byte chunks f = tid + 256 i of the tile.
-  // V: thread owns keys 4 kq .. 4 kq + 3 and head dims 8 dc .. 8 dc + 7.
+  // Staging roles.  K: thread loads 16-byte chunks f = tid + kThreads i of the tile.
+  // V: thread owns keys 2 kq, 2 kq + 1 and head dims 8 dc .. 8 dc + 7.
   // Loads are range-checked buffer loads whose descriptor starts at the tile's
   // first key: keys at or past kend_wg read as zeros, with no branch.
-  const int kq = tid & 15;
-  const int dc = tid >> 4;
+  const int kq = tid & 31;
+  const int dc = tid >> 5;
   const bool v_active = dc < D / 8;
   const int row_bytes = hkv * D * 2;
-  const int k_off = (tid / (D / 8)) * row_bytes + (tid % (D / 8)) * 16;  // + i * (256 / (D/8)) rows
-  const int v_off = 4 * kq * row_bytes + dc * 16;                         // + r rows
-  uint4 kreg[kKLoads], vreg[4];
+  const int k_off = (tid / (D / 8)) * row_bytes + (tid % (D / 8)) * 16;  // + i * (kThreads / (D/8)) rows
+  const int v_off = 2 * kq * row_bytes + dc * 16;                         // + r rows
+  uint4 kreg[kKLoads], vreg[2];
   auto tile_rsrc = [&](const bf16_t* base, int kb0) {
     const int left = (kend_wg - kb0 - 1) * row_bytes + D * 2;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base) + size_t(kb0) * key_stride, (short)0,
                                              left > 0 ? left : 0, kRsrcWord3);
   };
-  auto load_tile = [&](int kb0) {
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k_base, kb0);
+  auto load_k = [&](int tile) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k_base, tile * kBN);
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i)
       kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rk, k_off + i * (256 / (D / 8)) * row_bytes, 0, 0));
+                                              rk, k_off + i * (kThreads / (D / 8)) * row_bytes, 0, 0));
+  };
+  auto load_v = [&](int tile) {
     if (v_active) {
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v_base, kb0);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v_base, tile * kBN);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 2; ++r)
         vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + r * row_bytes, 0, 0));
     }
   };
-  auto store_tile = [&]() {
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
-      const int f = tid + 256 * i;
+      const int f = tid + kThreads * i;
       const int r = f / (D / 8);
       const int c = f % (D / 8);
-      *reinterpret_cast<uint4*>(k_lds + r * kKStride + c * 16) = kreg[i];
+      *reinterpret_cast<uint4*>(k_lds[buf] + r * kKStride + c * 16) = kreg[i];
     }
+  };
+  auto store_v = [&](int buf) {  // transposed: V^T rows are head dims
     if (v_active) {
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
         const int u = dd >> 1;
         const uint32_t w0 = u4_get(vreg[0], u), w1 = u4_get(vreg[1], u);
-        const uint32_t w2 = u4_get(vreg[2], u), w3 = u4_get(vreg[3], u);
-        uint2 out;
-        out.x = (dd & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
-        out.y = (dd & 1) ? pack_hi16(w2, w3) : pack_lo16(w2, w3);
-        *reinterpret_cast<uint2*>(v_lds + (8 * dc + dd) * kVStride + 8 * kq) = out;
+        *reinterpret_cast<uint32_t*>(v_lds[buf] + (8 * dc + dd) * kVStride + 4 * kq) =
+            (dd & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
       }
     }
   };
@@ -172,20 +174,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
   const float c = p.scale_log2;
   const int arow = perm_row(l32);
 
-  load_tile(0);
-  for (int it = 0; it < n_tiles; ++it) {
-    __syncthreads();  // all waves are done with the previous tile
-    store_tile();
-    __syncthreads();
-    const int kb0 = it * kBN;
-    if (it + 1 < n_tiles) load_tile(kb0 + kBN);
-    if (kb0 >= kend_w) continue;  // nothing visible to this wave here
-
-    // ---- S^T for 2 blocks of 32 keys (the first k-step starts from a zero accumulator)
-    f32x16_t s[2];
+  // S^T of one tile: 2 blocks of 32 keys, the first k-step from a zero accumulator.
+  auto qk = [&](int buf, f32x16_t* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t* arow_p = k_lds + (32 * kb + arow) * kKStride + 16 * half;
+      const uint8_t* arow_p = k_lds[buf] + (32 * kb + arow) * kKStride + 16 * half;
 #pragma unroll
       for (int kd = 0; kd < kKD; ++kd) {
         const uint4 a = *reinterpret_cast<const uint4*>(arow_p + 32 * kd);
@@ -194,36 +187,40 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
                                                         kd == 0 ? f32x16_t{} : s[kb], 0, 0, 0);
       }
     }
-    // Score register r of block kb belongs to key kb0 + 32 kb + 8 half + (r & 7) + 16 (r >> 3).
+  };
+  // Keys past a query's position get score -inf.  Only tiles that reach past
+  // the wave's first query need it; a tile wholly past every query of the wave
+  // masks to -inf throughout and contributes exact zeros.
+  auto mask = [&](int t, f32x16_t* s) {
+    const int kb0 = t * kBN;
     if (kb0 + kBN - 1 > start + qw0) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+          // score register r of block kb belongs to key kb0 + 32 kb + 8 half + (r & 7) + 16 (r >> 3)
           const int key = kb0 + 32 * kb + 8 * half + (r & 7) + 16 * (r >> 3);
           s[kb][r] = key > my_pos ? -INFINITY : s[kb][r];
         }
     }
+  };
+  // Softmax of one tile's (masked) scores into the bfloat16 B operands of P*V,
+  // without branches so that it interleaves with the next tile's score MFMAs.
+  // Lazy maximum: m is raised only when a score exceeds it by more than 2^8
+  // (wave-uniform decision); the rescale of o and l that this needs is done by
+  // the caller.  Returns the tile's sum of rounded probabilities in lt.
+  auto softmax = [&](const f32x16_t* s, uint4* pf, float& lt, float& alpha, bool& raised) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // this query's tile max, log2 units (finite: key 0 is visible)
-    // Lazy maximum: m is raised (and o, l rescaled) only when a score exceeds it
-    // by more than 2^8; otherwise probabilities up to 2^8 are accumulated as they
-    // are.  The decision is wave-uniform.
-    if (__ballot(mx > m + kLazyLog2)) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);  // 0 on the first visible tile (m = -inf)
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < kDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    uint4 pf[4];  // B operands of the 4 k-steps of 16 keys
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // this query's tile max, log2 units
+    raised = __ballot(mx > m + kLazyLog2) != 0;
+    const float m_new = raised ? fmaxf(m, mx) : m;
+    alpha = fast_exp2(m - m_new);  // 1 when unchanged; 0 on the first tile (m = -inf)
+    m = m_new;
+    lt = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -234,22 +231,79 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillParams p) {
           const float p0 = fast_exp2(fmaf(s[kb][8 * hh + 2 * j], c, -m));
           const float p1 = fast_exp2(fmaf(s[kb][8 * hh + 2 * j + 1], c, -m));
           w[j] = pack_bf16x2(p0, p1);
-          l = dot2_bf16(w[j], kBf16One2, l);  // the sum of the rounded probabilities P*V uses
+          lt = dot2_bf16(w[j], kBf16One2, lt);  // the sum of the rounded probabilities P*V uses
         }
         pf[2 * kb + hh] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
-    // ---- O^T += V^T P^T
+  };
+  // O^T += V^T P^T for one tile.
+  auto pv = [&](int buf, const uint4* pf) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        const uint4 a = *reinterpret_cast<const uint4*>(v_lds + (32 * db + l32) * kVStride + 32 * ks + 16 * half);
+        const uint4 a = *reinterpret_cast<const uint4*>(v_lds[buf] + (32 * db + l32) * kVStride + 32 * ks + 16 * half);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                         __builtin_bit_cast(bf16x8_t, pf[ks]), o[db], 0, 0, 0);
       }
     }
+  };
+
+  // Software pipeline over the workgroup's tiles.  Entering iteration t (after
+  // a barrier): K(t+1) sits in k_lds[(t+1)&1], V(t) in v_lds[t&1], the masked
+  // S(t) in registers, and the staging registers hold K(t+2) and V(t+1).  The
+  // iteration issues the score MFMAs of tile t+1 alongside the softmax of tile
+  // t (one branch-free block), stores K(t+2) and V(t+1) into the buffers the
+  // last barrier freed, starts the loads of K(t+3) and V(t+2), and accumulates
+  // P(t) V(t): one barrier per tile.  Loads past the last tile read zeros (the
+  // range check), so every step runs unconditionally.
+  auto step = [&](int t, f32x16_t* s_cur, f32x16_t* s_next) {
+    uint4 pf[4];  // B operands of the 4 k-steps of 16 keys
+    float lt, alpha;
+    bool raised;
+    qk((t + 1) & 1, s_next);
+    softmax(s_cur, pf, lt, alpha, raised);
+    // Keep the softmax in the block of the score MFMAs it overlaps with: an
+    // empty asm that consumes its results stops the compiler from sinking the
+    // exponentials past the branches below, next to their P*V use.
+    asm volatile("" ::"v"(pf[0].x), "v"(pf[0].y), "v"(pf[0].z), "v"(pf[0].w), "v"(pf[1].x), "v"(pf[1].y),
+                 "v"(pf[1].z), "v"(pf[1].w), "v"(pf[2].x), "v"(pf[2].y), "v"(pf[2].z), "v"(pf[2].w), "v"(pf[3].x),
+                 "v"(pf[3].y), "v"(pf[3].z), "v"(pf[3].w), "v"(lt));
+    if (raised) {
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    l += lt;
+    store_k(t & 1);
+    store_v((t + 1) & 1);
+    load_k(t + 3);
+    load_v(t + 2);
+    mask(t + 1, s_next);
+    pv(t & 1, pf);
+    __syncthreads();
+  };
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  load_k(1);
+  store_k(1);
+  load_v(1);
+  load_k(2);
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+  qk(0, sa);
+  mask(0, sa);
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
   }
+  if (t < n_tiles) step(t, sa, sb);
 
   // ---- normalise and store: o[db] register r holds head dim 32 db + 8 (r >> 2) + 4 half + (r & 3).
   const float l_tot = l + __shfl_xor(l, 32);
@@ -276,9 +330,9 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t s) {
   const long long n_wg = (long long)n_qt * p.n_q_heads * p.kv.batch;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.kv.head_dim == 128)
-    hipLaunchKernelGGL((prefill_mfma_kernel<128>), dim3(unsigned(n_wg)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<128>), dim3(unsigned(n_wg)), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<64>), dim3(unsigned(n_wg)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<64>), dim3(unsigned(n_wg)), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
