@@ -271,6 +271,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
                  "v"(pf[1].z), "v"(pf[1].w), "v"(pf[2].x), "v"(pf[2].y), "v"(pf[2].z), "v"(pf[2].w), "v"(pf[3].x),
                  "v"(pf[3].y), "v"(pf[3].z), "v"(pf[3].w), "v"(lt));
     if (raised) {
+      // A real (wave-uniform) branch: without the asm the compiler if-converts
+      // this block and multiplies o by alpha = 1 on every tile.
+      asm volatile("");
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < kDB; ++db)
