@@ -34,6 +34,31 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 
+# HBM traffic per launch of a kernel, measured with rocprofv3 --pmc FETCH_SIZE /
+# WRITE_SIZE and scaled by a known-size copy; valid only for the kernel sources
+# it was measured on (their SHA-256 is stored beside the figure).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "kv_cache_attention_kvcache_amd", "csrc")
+
+
+def source_digest(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name: str):
+    """Bytes per launch recorded for `name`, or None if absent or its sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)[name]
+        return rec["bytes_per_launch"] if rec["source_sha256"] == source_digest(rec["sources"]) else None
+    except (OSError, KeyError, ValueError):
+        return None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -204,7 +229,8 @@ def main():
         "phase_ms": {k: round(v, 3) for k, v in ph.items()},
         "roofline": {"bound": "hbm", "kernel": "decode (decode_bf16_kernel + decode_bf16_combine_kernel), batch 8",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("decode_bf16_b8_72k"),
                      "bytes_per_launch": int(per_launch_bytes), "avg_launch_us": round(avg_launch_ms * 1e3, 2)},
         "roofline_prefill": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": round(pre_tflops, 1),
                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
