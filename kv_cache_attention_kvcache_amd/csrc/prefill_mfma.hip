@@ -38,7 +38,7 @@ constexpr int kBM = 256;  // queries per workgroup (8 waves x 32)
 constexpr int kBN = 64;   // keys per tile
 constexpr int kWQ = 32;   // queries per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data format (gfx9 family)
-constexpr float kLazyLog2 = 8.f;  // probabilities may reach 2^8 before the running max is raised
+constexpr float kLazyBound = 256.f;  // probabilities may reach 2^8 before the running max is raised
 constexpr uint32_t kBf16One2 = 0x3F803F80u;  // (1.0, 1.0) as a bfloat16 pair
 
 // 2^x on the transcendental unit, without the denormal-result fix-up of exp2f:
@@ -204,22 +204,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
         }
     }
   };
-  // Softmax of one tile's (masked) scores into the bfloat16 B operands of P*V,
-  // without branches so that it interleaves with the next tile's score MFMAs.
-  // Lazy maximum: m is raised only when a score exceeds it by more than 2^8
-  // (wave-uniform decision); the rescale of o and l that this needs is done by
-  // the caller.  Returns the tile's sum of rounded probabilities in lt.
-  auto softmax = [&](const f32x16_t* s, uint4* pf, float& lt, float& alpha, bool& raised) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // this query's tile max, log2 units
-    raised = __ballot(mx > m + kLazyLog2) != 0;
-    const float m_new = raised ? fmaxf(m, mx) : m;
-    alpha = fast_exp2(m - m_new);  // 1 when unchanged; 0 on the first tile (m = -inf)
-    m = m_new;
+  // Probabilities of one tile's (masked) scores against the running maximum
+  // m, as the bfloat16 B operands of P*V, and the sum of the rounded values
+  // in lt.  Branch-free, so that it interleaves with the next tile's score
+  // MFMAs.  No per-tile maximum is taken first: the caller checks lt instead.
+  auto probs = [&](const f32x16_t* s, uint4* pf, float& lt) {
     lt = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -236,6 +225,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
         pf[2 * kb + hh] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
+  };
+  // Lazy maximum: m is raised only when a probability would exceed 2^8, which
+  // the row sum lt reveals (it bounds every term; it is inf or NaN on the first
+  // tile, where m = -inf).  Then the tile's true maximum is taken and the
+  // probabilities are recomputed; returns the factor that rescales o and l.
+  auto raise_max = [&](const f32x16_t* s, uint4* pf, float& lt) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // this query's tile max, log2 units
+    const float m_new = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - m_new);  // 0 on the first tile (m = -inf)
+    m = m_new;
+    probs(s, pf, lt);
+    return alpha;
   };
   // O^T += V^T P^T for one tile.
   auto pv = [&](int buf, const uint4* pf) {
@@ -260,20 +266,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
   // range check), so every step runs unconditionally.
   auto step = [&](int t, f32x16_t* s_cur, f32x16_t* s_next) {
     uint4 pf[4];  // B operands of the 4 k-steps of 16 keys
-    float lt, alpha;
-    bool raised;
+    float lt;
     qk((t + 1) & 1, s_next);
-    softmax(s_cur, pf, lt, alpha, raised);
+    probs(s_cur, pf, lt);
     // Keep the softmax in the block of the score MFMAs it overlaps with: an
     // empty asm that consumes its results stops the compiler from sinking the
     // exponentials past the branches below, next to their P*V use.
     asm volatile("" ::"v"(pf[0].x), "v"(pf[0].y), "v"(pf[0].z), "v"(pf[0].w), "v"(pf[1].x), "v"(pf[1].y),
                  "v"(pf[1].z), "v"(pf[1].w), "v"(pf[2].x), "v"(pf[2].y), "v"(pf[2].z), "v"(pf[2].w), "v"(pf[3].x),
                  "v"(pf[3].y), "v"(pf[3].z), "v"(pf[3].w), "v"(lt));
-    if (raised) {
+    if (__ballot(!(lt <= kLazyBound)) != 0) {
       // A real (wave-uniform) branch: without the asm the compiler if-converts
       // this block and multiplies o by alpha = 1 on every tile.
       asm volatile("");
+      const float alpha = raise_max(s_cur, pf, lt);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < kDB; ++db)
