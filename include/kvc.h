@@ -167,6 +167,40 @@ int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, v
                      int32_t T, int32_t n_q_heads, float scale, int32_t* dev_err, void* stream);
 
 /*
+ * kvc_decode_step -- one decode token per row in a single launch: RoPE of the
+ * new q and k at the row's position, in-place append of k and v, and
+ * attention of the rotated queries over keys 0..P (P = seqlens[b], the new
+ * key included).  No workspace.
+ *
+ * For small shapes, where a decode step is bound by kernel launches rather
+ * than arithmetic (Tiny-GPT post, "Why the GPU Shrugs"), and after the
+ * nanochat post ("What the KV cache looks like on disk"): the new K/V slices
+ * are written in place and attention runs against the full cache in one
+ * kernel launch.  The result equals kvc_rope_append (T = 1, same rope_base)
+ * followed by kvc_attn_decode, up to the order of float32 additions; the K/V
+ * bytes written into slot P are identical to kvc_rope_append's.  One
+ * workgroup handles one (row, KV head) and walks the row's keys itself, so
+ * this call suits short rows and small batches; long rows decode faster with
+ * kvc_rope_append + kvc_attn_decode, which spread a row over the whole GPU.
+ *
+ *   q        device, (batch, 1, n_q_heads, head_dim), raw (unrotated) queries.
+ *   k_new    device, (batch, 1, n_kv_heads, head_dim), raw key.
+ *   v_new    device, same shape, value.
+ *   out      device, (batch, 1, n_q_heads, head_dim).  May alias q: each
+ *            workgroup reads its query heads before it writes them.
+ *   scale    softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *   rope_base  RoPE base (10000 in the pages' workloads); must be > 1.
+ *
+ * n_q_heads / n_kv_heads must not exceed 16 (KVC_E_SHAPE).  seqlens is read,
+ * never written: the caller advances it after every layer of the step.  Rows
+ * with P < 0 or P + 1 > max_seq are skipped (KVC_DEV_CAPACITY): nothing is
+ * written for them.
+ */
+int kvc_decode_step(const kvc_cache* cache, int32_t layer, const void* q, const void* k_new,
+                    const void* v_new, void* out, int32_t n_q_heads, float scale, float rope_base,
+                    int32_t* dev_err, void* stream);
+
+/*
  * kvc_prefill_clone -- copy a batch-1 prefill into every row of an empty
  * batch-N cache (nanochat post, "The prefill trick, 12 lines").
  *

@@ -32,7 +32,7 @@ KVC_DEV_NOT_EMPTY = 2
 KVC_DEV_SRC_LEN = 4
 
 EXPORTS = ("kvc_rope_append", "kvc_decode_workspace_bytes", "kvc_attn_decode", "kvc_attn_prefill",
-           "kvc_prefill_clone", "kvc_status_string")
+           "kvc_decode_step", "kvc_prefill_clone", "kvc_status_string")
 
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 
@@ -57,6 +57,8 @@ def _load():
     lib.kvc_attn_decode.restype = ctypes.c_int
     lib.kvc_attn_prefill.argtypes = [cp, I32, P, P, I32, I32, F32, P, P]
     lib.kvc_attn_prefill.restype = ctypes.c_int
+    lib.kvc_decode_step.argtypes = [cp, I32, P, P, P, P, I32, F32, F32, P, P]
+    lib.kvc_decode_step.restype = ctypes.c_int
     lib.kvc_prefill_clone.argtypes = [cp, I32, cp, P, P]
     lib.kvc_prefill_clone.restype = ctypes.c_int
     lib.kvc_status_string.argtypes = [ctypes.c_int]
@@ -200,6 +202,22 @@ def kvc_attn_prefill(cache: KVCache, layer: int, q_rot, out=None, scale: float =
     st = lib.kvc_attn_prefill(cache.desc(), int(layer), _ptr(q_rot), _ptr(out), int(t), int(hq), float(scale),
                               _ptr(dev_err), _stream(stream, cache.k.device))
     _check("kvc_attn_prefill", st)
+    return out
+
+
+def kvc_decode_step(cache: KVCache, layer: int, q, k_new, v_new, out=None, scale: float = 0.0,
+                    rope_base: float = 10000.0, dev_err=None, stream=None):
+    """RoPE + append + decode attention for one new token per row in one launch; returns out."""
+    b, t, hq, d = q.shape
+    _like(q, cache, (cache.batch, 1, hq, cache.head_dim), "q")
+    _like(k_new, cache, (cache.batch, 1, cache.n_kv_heads, cache.head_dim), "k_new")
+    _like(v_new, cache, (cache.batch, 1, cache.n_kv_heads, cache.head_dim), "v_new")
+    if out is None:
+        out = torch.empty_like(q)
+    _like(out, cache, q.shape, "out")
+    st = lib.kvc_decode_step(cache.desc(), int(layer), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), int(hq),
+                             float(scale), float(rope_base), _ptr(dev_err), _stream(stream, cache.k.device))
+    _check("kvc_decode_step", st)
     return out
 
 

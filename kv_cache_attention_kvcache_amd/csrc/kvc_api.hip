@@ -227,6 +227,33 @@ int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, v
   return launch_status(kvc::launch_split_attention(p, s));
 }
 
+int kvc_decode_step(const kvc_cache* cache, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                    void* out, int32_t n_q_heads, float scale, float rope_base, int32_t* dev_err, void* stream) {
+  int st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (layer < 0 || layer >= cache->n_layers) return KVC_E_ARG;
+  if (!q || !k_new || !v_new || !out) return KVC_E_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return KVC_E_ARG;
+  if (!(rope_base > 1.f) || isinf(rope_base)) return KVC_E_ARG;
+  if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
+  if (n_q_heads / cache->n_kv_heads > kvc::kDecodeStepMaxGroup) return KVC_E_SHAPE;
+  if (int64_t(cache->batch) * cache->n_kv_heads > 0x7fffffffLL) return KVC_E_SHAPE;
+  float sc;
+  if (!resolve_scale(scale, cache->head_dim, &sc)) return KVC_E_ARG;
+  kvc::DecodeStepParams p;
+  p.kv = layer_view(cache, layer);
+  p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.out = out;
+  p.n_q_heads = n_q_heads;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  for (int i = 0; i < 64; ++i)
+    p.inv_freq[i] = i < cache->head_dim / 2 ? float(pow(double(rope_base), -2.0 * i / cache->head_dim)) : 0.f;
+  p.dev_err = dev_err;
+  return launch_status(kvc::launch_decode_step(p, static_cast<hipStream_t>(stream)));
+}
+
 int kvc_prefill_clone(const kvc_cache* src, int32_t src_len, const kvc_cache* dst, int32_t* dev_err,
                       void* stream) {
   int st = check_cache(src);

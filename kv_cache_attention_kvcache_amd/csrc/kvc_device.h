@@ -40,6 +40,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          acc, false);
 }
 
+// One RoPE pair rotation in float32 (half-split pairs i and i + D/2):
+// (x, y) -> (x c - y s, x s + y c).  Every kernel that rotates uses this one
+// expression, so that they all round the same way.
+__device__ __forceinline__ void rope_pair(float x, float y, float c, float s, float& xr, float& yr) {
+  xr = x * c - y * s;
+  yr = x * s + y * c;
+}
+
 // Byte permute: pick bytes of {hi_src:lo_src} (lo_src = bytes 0..3, hi_src = bytes 4..7).
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);

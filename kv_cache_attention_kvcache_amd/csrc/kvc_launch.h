@@ -73,6 +73,22 @@ struct PrefillParams {
 };
 hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t s);
 
+// Fused decode step (T = 1): RoPE + append + attention over the whole row in
+// one launch, one workgroup per (row, KV head).
+struct DecodeStepParams {
+  LayerView kv;
+  const void* q;      // (batch, 1, n_q_heads, head_dim), raw
+  const void* k_new;  // (batch, 1, n_kv_heads, head_dim), raw
+  const void* v_new;
+  void* out;          // (batch, 1, n_q_heads, head_dim)
+  int32_t n_q_heads;
+  float scale_log2;
+  float inv_freq[64];
+  int32_t* dev_err;
+};
+constexpr int kDecodeStepMaxGroup = 16;  // query heads per KV head
+hipError_t launch_decode_step(const DecodeStepParams& p, hipStream_t s);
+
 struct CloneParams {
   LayerView src;  // layer 0 view; n_layers below
   LayerView dst;

@@ -89,10 +89,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendParams p) {
     const float c[4] = {c4.x, c4.y, c4.z, c4.w};
     const float s[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ra[j] = a[j] * c[j] - b2[j] * s[j];
-      rb[j] = a[j] * s[j] + b2[j] * c[j];
-    }
+    for (int j = 0; j < 4; ++j) rope_pair(a[j], b2[j], c[j], s[j], ra[j], rb[j]);
     Vec4<T>::store(dst + i0, ra);
     Vec4<T>::store(dst + i0 + HALF, rb);
   }

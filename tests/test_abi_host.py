@@ -33,7 +33,8 @@ def _declared():
 
 def test_header_declares_the_four_calls_and_helpers():
     assert _declared() == sorted(["kvc_rope_append", "kvc_decode_workspace_bytes", "kvc_attn_decode",
-                                  "kvc_attn_prefill", "kvc_prefill_clone", "kvc_status_string"])
+                                  "kvc_attn_prefill", "kvc_decode_step", "kvc_prefill_clone",
+                                  "kvc_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -136,3 +137,24 @@ def test_clone_validation(lib):
     assert L.kvc_prefill_clone(ctypes.byref(src), 10,
                                ctypes.byref(_desc(lib, batch=8, max_seq=100, dtype=lib.KVC_F32)), None,
                                None) == lib.KVC_E_DTYPE
+
+
+def test_decode_step_validation(lib):
+    L, d = lib.lib, _desc(lib)  # batch 3, 4 KV heads, head_dim 128, bfloat16
+    q = P(0x40000)
+    ok = (q, q, q, q, 16, 0.0, 1e4, None, None)
+    call = lambda desc, layer, *a: L.kvc_decode_step(ctypes.byref(desc), layer, *a)
+    assert call(d, 2, *ok) == lib.KVC_E_ARG                         # layer out of range
+    assert call(d, -1, *ok) == lib.KVC_E_ARG
+    assert call(d, 0, None, q, q, q, 16, 0.0, 1e4, None, None) == lib.KVC_E_ARG
+    assert call(d, 0, q, None, q, q, 16, 0.0, 1e4, None, None) == lib.KVC_E_ARG
+    assert call(d, 0, q, q, None, q, 16, 0.0, 1e4, None, None) == lib.KVC_E_ARG
+    assert call(d, 0, q, q, q, None, 16, 0.0, 1e4, None, None) == lib.KVC_E_ARG
+    assert call(d, 0, P(0x40004), q, q, q, 16, 0.0, 1e4, None, None) == lib.KVC_E_ARG  # misaligned
+    assert call(d, 0, q, q, q, q, 16, 0.0, 1.0, None, None) == lib.KVC_E_ARG     # rope base <= 1
+    assert call(d, 0, q, q, q, q, 16, 0.0, float("inf"), None, None) == lib.KVC_E_ARG
+    assert call(d, 0, q, q, q, q, 16, float("nan"), 1e4, None, None) == lib.KVC_E_ARG
+    assert call(d, 0, q, q, q, q, 6, 0.0, 1e4, None, None) == lib.KVC_E_SHAPE   # 6 % 4 != 0
+    assert call(d, 0, q, q, q, q, 4 * 17, 0.0, 1e4, None, None) == lib.KVC_E_SHAPE  # group of 17 > 16
+    assert call(_desc(lib, head_dim=96), 0, *ok) == lib.KVC_E_SHAPE
+    assert call(_desc(lib, dtype=7), 0, *ok) == lib.KVC_E_DTYPE
