@@ -16,6 +16,12 @@ attention TFLOP/s, tokens/s, a roofline record for the decode kernel pair
 oracle timed on a bounded sample of the same work.
 
     python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+
+`--workload tiny` instead times the two tiny fp32 workloads' decode steps
+(one attention layer at batch 1; the six-layer tiny GPT at batch 16), which
+are bound by kernel launches: per step through kvc_rope_append +
+kvc_attn_decode, through the single-launch kvc_decode_step, and through
+kvc_decode_step with the whole step captured once in a HIP graph and replayed.
 """
 from __future__ import annotations
 
@@ -63,6 +69,7 @@ def measured_traffic(name: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=["long_context", "tiny"], default="long_context")
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps per batch size (default 512)")
@@ -105,6 +112,8 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU "
               "by design and every figure it reports is one GPU's.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "tiny":
+        return bench_tiny(args)
     import kv_cache_attention_kvcache_amd as kvc
     import synth
 
@@ -248,6 +257,137 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, kv_bytes_tok, q_)
     print(json.dumps(res), flush=True)
+
+
+class _TinyModel:
+    """The tiny fp32 workloads' glue around the library: one attention layer
+    (x -> qkv -> attention -> out projection) or the six-layer GPT (pre-norm
+    RMSNorm, attention, 4x exact-GELU MLP, tied head).  `mode` picks how a
+    decode token reaches the cache: "unfused" (kvc_rope_append then
+    kvc_attn_decode) or "fused" (kvc_decode_step)."""
+
+    def __init__(self, kvc, w, gpt: bool, mode: str, dev):
+        import synth
+        self.kvc, self.gpt, self.mode = kvc, gpt, mode
+        self.c, self.hq, self.d = w.extra["d_model"], w.n_q_heads, w.head_dim
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).float().to(dev)
+        if gpt:
+            self.n_layers, self.eps = w.extra["n_layers"], w.extra["rms_eps"]
+            self.wt = {n: to(a) for n, a in synth.tiny_gpt_weights(w).items()}
+            batch = w.extra["batch"]
+        else:
+            self.n_layers, self.eps = 1, 0.0
+            w_qkv, w_out = synth.tiny_layer_weights(w)
+            self.wt = {"qkv0": to(w_qkv), "out0": to(w_out)}
+            batch = 1
+        self.cache = kvc.KVCache.empty(self.n_layers, batch, w.max_seq, w.n_kv_heads, self.d,
+                                       dtype=torch.float32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def _norm(self, x):
+        return x * torch.rsqrt((x * x).mean(-1, keepdim=True) + self.eps)
+
+    def step(self, inp):
+        """GPT: token ids (B, T) -> logits (B, vocab); layer: x (1, T, C) -> y (1, T, C)."""
+        kvc, c, hq, d = self.kvc, self.c, self.hq, self.d
+        x = self.wt["emb"][inp] if self.gpt else inp
+        b, t = x.shape[0], x.shape[1]
+        for layer in range(self.n_layers):
+            h = self._norm(x) if self.gpt else x
+            qkv = h @ self.wt[f"qkv{layer}"]
+            q, k, v = (qkv[..., i * c:(i + 1) * c].reshape(b, t, hq, d).contiguous() for i in range(3))
+            if t == 1 and self.mode == "fused":
+                o = kvc.kvc_decode_step(self.cache, layer, q, k, v, dev_err=self.err)
+            else:
+                q_rot = kvc.kvc_rope_append(self.cache, layer, q, k, v, dev_err=self.err)
+                o = kvc.kvc_attn_prefill(self.cache, layer, q_rot, dev_err=self.err) if t > 1 else \
+                    kvc.kvc_attn_decode(self.cache, layer, q_rot, dev_err=self.err)
+            y = o.reshape(b, t, c) @ self.wt[f"out{layer}"]
+            if not self.gpt:
+                x = y
+                continue
+            x = x + y
+            hmid = torch.nn.functional.gelu(self._norm(x) @ self.wt[f"fc1{layer}"], approximate="none")
+            x = x + hmid @ self.wt[f"fc2{layer}"]
+        self.cache.seqlens += t
+        return self._norm(x[:, -1]) @ self.wt["emb"].T if self.gpt else x
+
+
+def bench_tiny(args):
+    """Decode steps of the two tiny fp32 workloads, three ways; one JSON line."""
+    import kv_cache_attention_kvcache_amd as kvc
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    torch.backends.cuda.matmul.allow_tf32 = False
+    K = max(1, args.steps)
+    out = {}
+    for name, w, gpt in (("tiny_layer", synth.TINY_LAYER, False), ("tiny_gpt6", synth.TINY_GPT6, True)):
+        n_prompt, n_steps = w.extra["prompt"], w.extra["steps"]
+        if gpt:
+            prompt = torch.from_numpy(synth.tiny_gpt_prompt(w)).to(dev)
+        else:
+            xs = torch.from_numpy(synth.tiny_layer_inputs(w)[0]).float().to(dev)[None]  # (1, 256, C)
+            prompt = xs[:, :n_prompt].contiguous()
+            dec_in = [xs[:, n_prompt + s:n_prompt + s + 1].contiguous() for s in range(n_steps)]
+        batch = prompt.shape[0]
+        res = {}
+        for mode in ("unfused", "fused", "fused_graph"):
+            m = _TinyModel(kvc, w, gpt, "fused" if mode == "fused_graph" else mode, dev)
+            static_in = torch.zeros((batch, 1), dtype=torch.int64, device=dev) if gpt else \
+                torch.zeros((1, 1, m.c), dtype=torch.float32, device=dev)
+            graph, static_out = None, None
+            if mode == "fused_graph":
+                # warm up the glue on a side stream, then capture one decode step
+                m.step(prompt)
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    for _ in range(2):
+                        m.step(static_in)
+                torch.cuda.current_stream().wait_stream(side)
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    static_out = m.step(static_in)
+            times = []
+            for rep in range(args.warmup + K):
+                m.cache.seqlens.zero_()
+                last = m.step(prompt)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for s in range(n_steps):
+                    nxt = last.argmax(dim=1)[:, None] if gpt else dec_in[s]
+                    if graph is not None:
+                        static_in.copy_(nxt)
+                        graph.replay()
+                        last = static_out
+                    else:
+                        last = m.step(nxt)
+                e1.record()
+                torch.cuda.synchronize()
+                if rep >= args.warmup:
+                    times.append(e0.elapsed_time(e1))
+            assert m.err.item() == 0, f"{name} {mode}: device error bits {m.err.item()}"
+            ms = sorted(times)[len(times) // 2]
+            res[mode] = {"us_per_step": round(ms * 1e3 / n_steps, 2),
+                         "tokens_per_s": round(batch * n_steps / (ms * 1e-3), 1),
+                         "launches_per_step_attention": m.n_layers * (1 if mode != "unfused" else 2)}
+            log(f"{name} {mode}: {res[mode]}", args.quiet)
+        out[name] = {"batch": batch, "layers": w.extra["n_layers"] if gpt else 1,
+                     "decode_steps": n_steps, **res}
+    g = out["tiny_gpt6"]
+    print(json.dumps({
+        "metric": "tiny GPT decode tokens/s (6 layers, batch 16, fp32)",
+        "value": g["fused_graph"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(g["fused_graph"]["us_per_step"] / 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "tiny_gpt6_fp32 and tiny_layer_fp32 decode", "prompt": 8, "decode_steps": 248,
+                   "parallelism": "none"},
+        "roofline": {"bound": "launch", "note": "a few microseconds of GPU work per step: the step time is "
+                     "launch and glue latency, so a bandwidth or MFMA fraction is not meaningful here"},
+        "workloads": out}), flush=True)
 
 
 class _Null:

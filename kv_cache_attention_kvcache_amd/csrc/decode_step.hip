@@ -15,7 +15,9 @@
 //      the value written to slot P; the rounded queries kept in LDS;
 //   2. keys 0..P in tiles of 256: thread = key for the scores, an online
 //      softmax per head (wave reductions, then across the 4 waves through
-//      LDS), thread = (head, dim) for the weighted sum of V.
+//      LDS); for the weighted sum of V wave w takes every fourth key of the
+//      tile and lane l the head dims l, l + 64, for all G heads at once; the
+//      four waves' sums are added in a fixed order at the end.
 // The slot this workgroup wrote is read back by it after a barrier.
 #include "kvc_device.h"
 #include "kvc_launch.h"
@@ -54,11 +56,12 @@ __device__ __forceinline__ void load8(const bf16_t* p, float* x) {
 template <typename T, int D, int GB>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeStepParams p) {
   constexpr int HALF = D / 2;
-  constexpr int kOut = (GB * D + kThreads - 1) / kThreads;  // (head, dim) outputs per thread
+  constexpr int kDU = D / kWave;  // head dims per lane in the weighted sum of V
   __shared__ float cs[HALF], sn[HALF];
   __shared__ __align__(16) float qs[GB][D];     // rotated, rounded queries
   __shared__ float pr[GB][kTile];               // one tile's probabilities
   __shared__ float red[kWaves][GB];             // per-wave partial max / sum
+  __shared__ float part[kWaves][GB][D];         // per-wave sums of V, folded at the end
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -114,14 +117,14 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeStepParams 
   const size_t key_stride = size_t(hkv) * D;
   const T* k_base = static_cast<const T*>(p.kv.k) + size_t(b) * p.kv.max_seq * key_stride + size_t(g) * D;
   const T* v_base = static_cast<const T*>(p.kv.v) + size_t(b) * p.kv.max_seq * key_stride + size_t(g) * D;
-  float m_run[GB], l_run[GB], acc[kOut];
+  float m_run[GB], l_run[GB], acc[GB][kDU];
 #pragma unroll
   for (int h = 0; h < GB; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.f;
-  }
 #pragma unroll
-  for (int r = 0; r < kOut; ++r) acc[r] = 0.f;
+    for (int u = 0; u < kDU; ++u) acc[h][u] = 0.f;
+  }
 
   for (int j0 = 0; j0 < n_keys; j0 += kTile) {
     const int j = j0 + tid;
@@ -181,38 +184,46 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeStepParams 
       l_run[h] = l_run[h] * alpha[h] + lt;
       m_run[h] = m_new[h];
     }
-    // Weighted sum of V: thread owns outputs o = tid + 256 r, head o / D, dim o % D.
+    // Weighted sum of V: this wave's keys i = wave, wave + 4, ... of the tile,
+    // this lane's head dims lane + 64 u, every head of the group.
     const int n_in = min(kTile, n_keys - j0);
 #pragma unroll
-    for (int r = 0; r < kOut; ++r) {
-      const int o = tid + kThreads * r;
-      const int h = o / D;
-      if (h < G) {
-        const int d = o - h * D;
-        float a = 0.f;
-        const T* vcol = v_base + size_t(j0) * key_stride + d;
-        for (int i = 0; i < n_in; ++i) a = fmaf(pr[h][i], to_f(vcol[size_t(i) * key_stride]), a);
-        float al = alpha[0];
+    for (int h = 0; h < GB; ++h)
 #pragma unroll
-        for (int hh = 1; hh < GB; ++hh) al = hh == h ? alpha[hh] : al;
-        acc[r] = acc[r] * al + a;
+      for (int u = 0; u < kDU; ++u) acc[h][u] *= alpha[h];
+    const T* vrow = v_base + size_t(j0) * key_stride + lane;
+#pragma unroll 4
+    for (int i = wave; i < n_in; i += kWaves) {
+      float vv[kDU];
+#pragma unroll
+      for (int u = 0; u < kDU; ++u) vv[u] = to_f(vrow[size_t(i) * key_stride + kWave * u]);
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        if (h < G) {
+          const float ph = pr[h][i];
+#pragma unroll
+          for (int u = 0; u < kDU; ++u) acc[h][u] = fmaf(ph, vv[u], acc[h][u]);
+        }
       }
     }
     __syncthreads();  // pr and red are rewritten by the next tile
   }
 
-  // ---- normalise and store.
+  // ---- fold the four waves' sums (fixed order), normalise and store.
 #pragma unroll
-  for (int r = 0; r < kOut; ++r) {
-    const int o = tid + kThreads * r;
+  for (int h = 0; h < GB; ++h)
+    if (h < G)
+#pragma unroll
+      for (int u = 0; u < kDU; ++u) part[wave][h][lane + kWave * u] = acc[h][u];
+  __syncthreads();
+  for (int o = tid; o < G * D; o += kThreads) {
     const int h = o / D;
-    if (h < G) {
-      const int d = o - h * D;
-      float lr = l_run[0];
+    const int d = o - h * D;
+    const float sum = (part[0][h][d] + part[1][h][d]) + (part[2][h][d] + part[3][h][d]);
+    float lr = l_run[0];
 #pragma unroll
-      for (int hh = 1; hh < GB; ++hh) lr = hh == h ? l_run[hh] : lr;
-      static_cast<T*>(p.out)[(size_t(b) * hq + g * G + h) * D + d] = from_f<T>(acc[r] / lr);
-    }
+    for (int hh = 1; hh < GB; ++hh) lr = hh == h ? l_run[hh] : lr;
+    static_cast<T*>(p.out)[(size_t(b) * hq + g * G + h) * D + d] = from_f<T>(sum / lr);
   }
 }
 
