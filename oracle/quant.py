@@ -49,3 +49,39 @@ def quantize_int8(x):
 def dequantize_int8(codes, scales) -> np.ndarray:
     """codes * scale per vector, float64 (exact: an int8 times a float32 fits float64)."""
     return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def appended_slots_int8(k_raw, v_raw, start: int, base: float = 10000.0):
+    """What an append into an int8 cache writes for one row's T tokens at start..start+T-1.
+
+    k_raw, v_raw: (T, Hkv, D) raw values.  The key is rotated at its position
+    and rounded to bfloat16, the value rounded to bfloat16 (what a bfloat16
+    cache would hold), and each (token, head) vector is then quantized.
+    Returns (k_codes, k_scales, v_codes, v_scales).
+    """
+    from .attention import appended_slots
+    k_hat, v_hat = appended_slots(k_raw, v_raw, start, "bf16", base)
+    kc, ks = quantize_int8(k_hat)
+    vc, vs = quantize_int8(v_hat)
+    return kc, ks, vc, vs
+
+
+def decode_over_int8(k_codes, k_scales, v_codes, v_scales, q_raw, k_raw, v_raw, base: float = 10000.0,
+                     scale: float | None = None) -> np.ndarray:
+    """One decode token over a row whose first P positions hold int8 codes and scales.
+
+    k_codes/v_codes (P, Hkv, D), k_scales/v_scales (P, Hkv): the stored
+    (already rotated) history.  q_raw (Hq, D), k_raw/v_raw (Hkv, D): the new
+    token at position P, whose key and value are quantized as the append
+    stores them.  The query is rotated and rounded to bfloat16 only.
+    Attention in float64 over the dequantized keys and values.  Returns (Hq, D).
+    """
+    from .attention import attend
+    from .numerics import round_to
+    from .rope import rotate_round
+    p = np.asarray(k_codes).shape[0]
+    kc, ks, vc, vs = appended_slots_int8(np.asarray(k_raw)[None], np.asarray(v_raw)[None], p, base)
+    k_all = np.concatenate([dequantize_int8(k_codes, k_scales), dequantize_int8(kc, ks)], axis=0)
+    v_all = np.concatenate([dequantize_int8(v_codes, v_scales), dequantize_int8(vc, vs)], axis=0)
+    q_hat = rotate_round(round_to(np.asarray(q_raw)[None], "bf16"), [p], "bf16", base)
+    return attend(q_hat, k_all, v_all, [p], scale)[0]

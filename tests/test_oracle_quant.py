@@ -92,3 +92,29 @@ def test_error_bound_and_scale_invariance():
     # doubling a vector (exact in float32) doubles the scale and keeps every code
     codes2, scale2 = quant.quantize_int8(2.0 * x)
     assert np.array_equal(codes2, codes) and np.array_equal(scale2, 2 * scale)
+
+
+def test_int8_decode_is_bf16_decode_on_dequantized_values():
+    """decode_over_int8 equals the bfloat16 decode oracle run on the dequantized history and on
+    the dequantized new key/value; and it differs from the unquantized decode by no more than
+    the quantization moves the values (a loose sanity bound)."""
+    from oracle import attention as oatt
+    from oracle import rope
+    g = np.random.default_rng(5)
+    p, hkv, hq, d = 37, 2, 4, 64
+    hist_k = numerics.round_bf16(g.standard_normal((p, hkv, d)))
+    hist_v = numerics.round_bf16(g.standard_normal((p, hkv, d)))
+    kc, ks = quant.quantize_int8(hist_k)
+    vc, vs = quant.quantize_int8(hist_v)
+    q, k, v = (g.standard_normal((n, d)).astype(np.float32) for n in (hq, hkv, hkv))
+    got = quant.decode_over_int8(kc, ks, vc, vs, q, k, v)
+    k_new = rope.rotate_round(numerics.round_bf16(k[None]), [p], "bf16")
+    nkc, nks = quant.quantize_int8(k_new)
+    nvc, nvs = quant.quantize_int8(numerics.round_bf16(v[None]))
+    k_all = np.concatenate([quant.dequantize_int8(kc, ks), quant.dequantize_int8(nkc, nks)])
+    v_all = np.concatenate([quant.dequantize_int8(vc, vs), quant.dequantize_int8(nvc, nvs)])
+    q_hat = rope.rotate_round(numerics.round_bf16(q[None]), [p], "bf16")
+    ref = oatt.attend(q_hat, k_all, v_all, [p])[0]
+    assert np.allclose(got, ref, rtol=0, atol=1e-13)
+    plain = oatt.decode_over_existing(hist_k, hist_v, q, k, v, "bf16")
+    assert 0 < np.max(np.abs(got - plain)) < 0.05
