@@ -23,6 +23,21 @@
  * KVC_F32 or KVC_BF16 (bfloat16, round to nearest even).  All accumulation
  * is in float32.  head_dim must be 64 or 128.
  *
+ * 8-bit cache (KVC_I8).  Cake paper, Section 5.1 ("Compression methods") and
+ * Section 5.5 (Table 6): the KV cache can be kept in 8 bits, which halves the
+ * bytes decode must stream.  K and V then hold int8 codes, and k_scale /
+ * v_scale hold one float32 scale per cached vector, shape
+ *     (n_layers, batch, max_seq, n_kv_heads).
+ * A vector x (the head_dim values of one position and KV head, as a bfloat16
+ * cache would hold them: the rotated key rounded to bfloat16, the value
+ * rounded to bfloat16) is stored as s = amax|x| / 127 and codes
+ * c_i = round_half_even(x_i / s) in [-127, 127] (float32 quotient; s = 0 and
+ * all codes 0 for an all-zero vector); it reads back as c_i * s.  q, out,
+ * k_new and v_new are bfloat16.  kvc_rope_append quantizes as it appends,
+ * kvc_attn_decode decodes from the codes, and kvc_prefill_clone copies codes
+ * and scales.  kvc_attn_prefill and kvc_decode_step do not take an 8-bit
+ * cache (KVC_E_DTYPE).
+ *
  * Errors.  A call first validates its arguments on the host; if that fails
  * it returns a negative KVC_E_* code and launches nothing, so nothing is
  * written.  Conditions that depend on device data (seqlens) are checked by
@@ -41,8 +56,8 @@
 extern "C" {
 #endif
 
-/* Element types of q, out, k_new, v_new and the cache. */
-enum { KVC_F32 = 0, KVC_BF16 = 1 };
+/* Element types of the cache (and of q, out, k_new, v_new: bfloat16 for KVC_I8). */
+enum { KVC_F32 = 0, KVC_BF16 = 1, KVC_I8 = 2 };
 
 /* Host-side status codes (return values). */
 enum {
@@ -72,7 +87,9 @@ typedef struct kvc_cache {
   int32_t max_seq;
   int32_t n_kv_heads;
   int32_t head_dim;
-  int32_t dtype;    /* KVC_F32 or KVC_BF16 */
+  int32_t dtype;    /* KVC_F32, KVC_BF16 or KVC_I8 */
+  float* k_scale;   /* KVC_I8 only: device, (n_layers, batch, max_seq, n_kv_heads); else ignored */
+  float* v_scale;   /* KVC_I8 only: device, same shape */
 } kvc_cache;
 
 /*

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
 KVC_F32 = 0
 KVC_BF16 = 1
+KVC_I8 = 2
 KVC_OK = 0
 KVC_E_ARG = -1
 KVC_E_SHAPE = -2
@@ -34,13 +35,14 @@ KVC_DEV_SRC_LEN = 4
 EXPORTS = ("kvc_rope_append", "kvc_decode_workspace_bytes", "kvc_attn_decode", "kvc_attn_prefill",
            "kvc_decode_step", "kvc_prefill_clone", "kvc_status_string")
 
-_DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
+_DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16, torch.int8: KVC_I8}
 
 
 class kvc_cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("seqlens", ctypes.c_void_p),
                 ("n_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("max_seq", ctypes.c_int32),
-                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 def _load():
@@ -96,26 +98,40 @@ def _stream(stream, device):
 class KVCache:
     """A cache whose buffers are caller-owned torch tensors.
 
-    k, v: (n_layers, batch, max_seq, n_kv_heads, head_dim), float32 or
-    bfloat16, contiguous, on one GPU; seqlens: (batch,) int32 on that GPU.
+    k, v: (n_layers, batch, max_seq, n_kv_heads, head_dim), float32,
+    bfloat16 or int8 (codes), contiguous, on one GPU; seqlens: (batch,) int32
+    on that GPU.  An int8 cache also takes k_scale, v_scale: float32
+    (n_layers, batch, max_seq, n_kv_heads), one scale per cached vector; its
+    queries and outputs are bfloat16.
     """
 
-    def __init__(self, k: torch.Tensor, v: torch.Tensor, seqlens: torch.Tensor):
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, seqlens: torch.Tensor, k_scale=None, v_scale=None):
         if k.shape != v.shape or k.dim() != 5 or k.dtype != v.dtype or k.dtype not in _DTYPE_CODE:
-            raise ValueError("k and v must be matching 5-d float32/bfloat16 tensors")
+            raise ValueError("k and v must be matching 5-d float32/bfloat16/int8 tensors")
         if not (k.is_contiguous() and v.is_contiguous()) or not (k.is_cuda and v.is_cuda):
             raise ValueError("k and v must be contiguous device tensors")
         if seqlens.dtype != torch.int32 or seqlens.shape != (k.shape[1],) or not seqlens.is_cuda:
             raise ValueError("seqlens must be an int32 (batch,) device tensor")
+        if k.dtype == torch.int8:
+            for sc in (k_scale, v_scale):
+                if sc is None or sc.dtype != torch.float32 or tuple(sc.shape) != tuple(k.shape[:4]) \
+                        or not sc.is_contiguous() or sc.device != k.device:
+                    raise ValueError("an int8 cache needs contiguous float32 k_scale and v_scale of shape "
+                                     "(n_layers, batch, max_seq, n_kv_heads) on its device")
         self.k, self.v, self.seqlens = k, v, seqlens
+        self.k_scale, self.v_scale = (k_scale, v_scale) if k.dtype == torch.int8 else (None, None)
         self._desc = kvc_cache(k.data_ptr(), v.data_ptr(), seqlens.data_ptr(), *[int(s) for s in k.shape],
-                               _DTYPE_CODE[k.dtype])
+                               _DTYPE_CODE[k.dtype],
+                               self.k_scale.data_ptr() if self.k_scale is not None else None,
+                               self.v_scale.data_ptr() if self.v_scale is not None else None)
 
     @classmethod
     def empty(cls, n_layers, batch, max_seq, n_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda"):
         shape = (n_layers, batch, max_seq, n_kv_heads, head_dim)
+        scales = (torch.zeros(shape[:4], dtype=torch.float32, device=device),
+                  torch.zeros(shape[:4], dtype=torch.float32, device=device)) if dtype == torch.int8 else (None, None)
         return cls(torch.empty(shape, dtype=dtype, device=device), torch.empty(shape, dtype=dtype, device=device),
-                   torch.zeros(batch, dtype=torch.int32, device=device))
+                   torch.zeros(batch, dtype=torch.int32, device=device), *scales)
 
     @property
     def n_layers(self):
@@ -139,6 +155,11 @@ class KVCache:
 
     @property
     def dtype(self):
+        """Element type of q, out, k_new and v_new for this cache (bfloat16 for an int8 cache)."""
+        return torch.bfloat16 if self.k.dtype == torch.int8 else self.k.dtype
+
+    @property
+    def storage_dtype(self):
         return self.k.dtype
 
     def desc(self):

@@ -6,7 +6,9 @@
 // vector of the source run once and writes it to every empty destination
 // row (read once, write N times: HBM-bound).  A second, one-workgroup kernel
 // then sets the destination lengths, so no block reads a length another
-// block may already have changed.
+// block may already have changed.  An int8 cache also has one float32 scale
+// per (position, KV head) for K and for V; those runs are copied the same way
+// (grid planes 2 and 3), 4 bytes at a time.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 #include "kvc.h"
@@ -15,18 +17,33 @@ namespace kvc {
 
 namespace {
 
+__device__ __forceinline__ size_t elem_bytes(int dtype) { return dtype == KVC_F32 ? 4 : dtype == KVC_BF16 ? 2 : 1; }
+
 __global__ __launch_bounds__(256) void clone_copy_kernel(CloneParams p) {
   if (p.src.seqlens[0] != p.src_len) return;  // reported by clone_lengths_kernel
   const int layer = blockIdx.y;
+  const int n_rows = p.dst.batch;
+  if (blockIdx.z >= 2) {  // scales of an int8 cache
+    const size_t n = size_t(p.src_len) * p.src.n_kv_heads;
+    const float* src = (blockIdx.z == 2 ? p.src.k_scale : p.src.v_scale) +
+                       size_t(layer) * p.src.max_seq * p.src.n_kv_heads;
+    float* dst0 = blockIdx.z == 2 ? p.dst.k_scale : p.dst.v_scale;
+    const size_t dst_row = size_t(p.dst.max_seq) * p.dst.n_kv_heads;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x) {
+      const float val = src[i];
+      for (int r = 0; r < n_rows; ++r)
+        if (p.dst.seqlens[r] == 0) dst0[(size_t(layer) * n_rows + r) * dst_row + i] = val;
+    }
+    return;
+  }
   const bool is_v = blockIdx.z != 0;
-  const size_t esz = p.src.dtype == KVC_BF16 ? 2 : 4;
+  const size_t esz = elem_bytes(p.src.dtype);
   const size_t tok_bytes = size_t(p.src.n_kv_heads) * p.src.head_dim * esz;
   const size_t n_vec = size_t(p.src_len) * tok_bytes / 16;
   const uint8_t* src = static_cast<const uint8_t*>(is_v ? p.src.v : p.src.k) +
                        size_t(layer) * p.src.max_seq * tok_bytes;  // source batch is 1
   uint8_t* dst0 = static_cast<uint8_t*>(is_v ? p.dst.v : p.dst.k);
   const size_t dst_row_bytes = size_t(p.dst.max_seq) * tok_bytes;
-  const int n_rows = p.dst.batch;
   for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_vec; i += size_t(gridDim.x) * blockDim.x) {
     const uint4 val = reinterpret_cast<const uint4*>(src)[i];
     for (int r = 0; r < n_rows; ++r) {
@@ -52,12 +69,13 @@ __global__ __launch_bounds__(256) void clone_lengths_kernel(CloneParams p) {
 }  // namespace
 
 hipError_t launch_clone(const CloneParams& p, hipStream_t s) {
-  const size_t esz = p.src.dtype == KVC_BF16 ? 2 : 4;
+  const size_t esz = p.src.dtype == KVC_F32 ? 4 : p.src.dtype == KVC_BF16 ? 2 : 1;
   const size_t n_vec = size_t(p.src_len) * p.src.n_kv_heads * p.src.head_dim * esz / 16;
   if (n_vec > 0) {
     const size_t want = (n_vec + 255) / 256;
     const unsigned gx = unsigned(want < 1024 ? want : 1024);
-    hipLaunchKernelGGL(clone_copy_kernel, dim3(gx, p.n_layers, 2), dim3(256), 0, s, p);
+    const unsigned planes = p.src.dtype == KVC_I8 ? 4 : 2;  // K, V (and their scales)
+    hipLaunchKernelGGL(clone_copy_kernel, dim3(gx, p.n_layers, planes), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

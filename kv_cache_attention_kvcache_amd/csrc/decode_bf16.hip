@@ -1,4 +1,4 @@
-// Split-KV flash-decode for bfloat16 caches, on vector ALUs (no MFMA).
+// Split-KV flash-decode for bfloat16 and int8 caches, on vector ALUs (no MFMA).
 //
 // Tiny-GPT post, Gotcha 2: a decode query sees every cached key.  nanochat
 // post ("What the KV cache looks like on disk"): attention runs against the
@@ -37,6 +37,15 @@
 //   * P*V: probabilities go to LDS as bfloat16 key pairs; V goes to LDS as
 //     key-pair-packed dims; each lane then owns head_dim/64 output dims of all
 //     GB heads and accumulates with v_dot2_f32_bf16 (two keys per product).
+//
+// int8 caches (Cake paper, Section 5.1 "Compression methods" and Section 5.5:
+// 8-bit quantization halves the bytes to move): a lane loads the 8 int8 codes
+// of its 8 head dims (8-byte loads, 8 lanes per 128-byte row) and widens them
+// to bfloat16 pairs, which hold every code exactly; everything after that is
+// the bfloat16 path.  Each lane also loads the float32 scales of the keys it
+// keeps after the reduction, with the tile: a key's K scale multiplies its
+// scores, its V scale multiplies the probability that weights its codes in
+// P*V, while the softmax sum takes the unscaled probability.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 #include "kvc.h"
@@ -51,6 +60,7 @@ constexpr float kLazyLog2 = 8.f;  // probabilities may reach 2^8 before the max 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 template <int D, int GB>
 struct Cfg {
@@ -127,6 +137,33 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int v
   return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, kCpolNT);
 }
 
+// What a lane loads of one K/V row (its 8 head dims) and how it becomes the
+// four bfloat16 pairs the dot products take.
+template <bool Q8>
+struct Elem;
+template <>
+struct Elem<false> {  // bfloat16: 16 bytes
+  typedef u32x4_t Raw;
+  static constexpr int kBytes = 2;
+  static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, int off) { return buffer_load16(r, off); }
+  static __device__ __forceinline__ u32x4_t widen(const Raw& w) { return w; }
+};
+template <>
+struct Elem<true> {  // int8 codes: 8 bytes, widened exactly (|code| <= 127 fits bfloat16's 8 significant bits)
+  typedef u32x2_t Raw;
+  static constexpr int kBytes = 1;
+  static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolNT);
+  }
+  static __device__ __forceinline__ uint32_t pair(uint32_t w, int byte) {
+    return pack_bf16x2(static_cast<float>(static_cast<int8_t>(w >> (8 * byte))),
+                       static_cast<float>(static_cast<int8_t>(w >> (8 * byte + 8))));
+  }
+  static __device__ __forceinline__ u32x4_t widen(const Raw& w) {
+    return u32x4_t{pair(w.x, 0), pair(w.x, 2), pair(w.y, 0), pair(w.y, 2)};
+  }
+};
+
 // Number of 32-key tiles of row b, or 0 if its length is out of range.
 __device__ __forceinline__ int row_tiles(const int32_t* seqlens, int b, int max_seq) {
   const int p = seqlens[b];
@@ -194,9 +231,11 @@ __device__ SegPos find_segment(const DecodeParams& p, int t, int lane) {
 // Flattened tile index w N / P where workgroup w's range starts.
 __device__ __forceinline__ int range_begin(long long w, int n, int n_wg) { return int(w * n / n_wg); }
 
-template <int D, int GB>
+template <int D, int GB, bool Q8>
 __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodeParams p) {
   using C = Cfg<D, GB>;
+  using E = Elem<Q8>;
+  using Raw = typename E::Raw;
   constexpr int LPR = C::LPR;
   __shared__ __align__(16) uint8_t smem[C::kLds];
 
@@ -215,14 +254,25 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
   const int hkv = p.kv.n_kv_heads;
   const int group = hq / hkv;
   const int spr = hkv * p.n_hb;
-  const int row_bytes = hkv * D * 2;  // bytes between consecutive positions of one head
+  const int row_bytes = hkv * D * E::kBytes;  // bytes between consecutive positions of one head
   const float c = p.scale_log2;
 
   uint8_t* vlds = smem + wave * C::kWaveLds;
   uint32_t* plds = reinterpret_cast<uint32_t*>(vlds + C::kVBytes);
 
   // Per-lane byte offset of slot s's row within a tile: row = 2 (s/2 * RPI + rg) + (s & 1).
-  const int lane_off = 2 * rg * row_bytes + x * 16;
+  const int lane_off = 2 * rg * row_bytes + x * 8 * E::kBytes;
+  // The slots a lane keeps after the row-splitting steps start at off_keep;
+  // their rows (for the int8 scales) are fixed for the whole call.
+  int off_keep = 0;
+#pragma unroll
+  for (int k = C::HB; k < C::S; ++k) off_keep += ((x >> (C::S - 1 - k)) & 1) * ((C::NR >> (k - C::HB)) / 2);
+  int sc_off[C::NRK];  // byte offset of kept row r's scale within a tile's scale run
+#pragma unroll
+  for (int r = 0; r < C::NRK; ++r) {
+    const int slot = r + off_keep;
+    sc_off[r] = (2 * ((slot >> 1) * C::RPI + rg) + (slot & 1)) * hkv * 4;
+  }
 
   SegPos seg = find_segment(p, t_begin, lane);
   int t = t_begin;
@@ -237,9 +287,11 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
     const int j0 = t - seg.base, j1 = run_end - seg.base;  // local tiles of the run
 
     // Segment bases (row b, position 0, KV head g).
-    const size_t elem0 = (size_t(seg.b) * p.kv.max_seq * hkv + g) * D;
-    const bf16_t* kseg = static_cast<const bf16_t*>(p.kv.k) + elem0;
-    const bf16_t* vseg = static_cast<const bf16_t*>(p.kv.v) + elem0;
+    const size_t vec0 = size_t(seg.b) * p.kv.max_seq * hkv + g;
+    const uint8_t* kseg = static_cast<const uint8_t*>(p.kv.k) + vec0 * D * E::kBytes;
+    const uint8_t* vseg = static_cast<const uint8_t*>(p.kv.v) + vec0 * D * E::kBytes;
+    const float* ksseg = Q8 ? p.kv.k_scale + vec0 : nullptr;
+    const float* vsseg = Q8 ? p.kv.v_scale + vec0 : nullptr;
 
     // Queries of this block in this lane's head order: slot h holds head h ^ gh(x), dims [8x, 8x+8).
     u32x4_t q[GB];
@@ -261,25 +313,37 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
 #pragma unroll
       for (int i = 0; i < C::DL; ++i) acc[h][i] = 0.f;
 
-    auto rsrc_at = [&](const bf16_t* base, int j) {
+    auto rsrc_at = [&](const uint8_t* base, int j) {
       const int key0 = j * kTileKeys;
-      const int left = (L - key0 - 1) * row_bytes + D * 2;  // valid bytes from the tile's first row
-      return __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<bf16_t*>(base) + size_t(key0) * hkv * D, (short)0, left > 0 ? left : 0, kRsrcWord3);
+      const int left = (L - key0 - 1) * row_bytes + D * E::kBytes;  // valid bytes from the tile's first row
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base) + size_t(key0) * row_bytes, (short)0,
+                                               left > 0 ? left : 0, kRsrcWord3);
     };
-    auto issue = [&](const bf16_t* base, int j, u32x4_t* buf) {
+    auto issue = [&](const uint8_t* base, int j, Raw* buf) {
       const __amdgpu_buffer_rsrc_t r = rsrc_at(base, j);
 #pragma unroll
       for (int s = 0; s < C::NR; ++s) {
         const int off = lane_off + (2 * (s >> 1) * C::RPI + (s & 1)) * row_bytes;
-        buf[s] = buffer_load16(r, off);
+        buf[s] = E::load(r, off);
+      }
+    };
+    // int8: the scales of this lane's kept rows of tile j (zeros past the row's length).
+    auto issue_sc = [&](const float* base, int j, float* buf) {
+      if constexpr (Q8) {
+        const int key0 = j * kTileKeys;
+        const int left = (L - key0 - 1) * hkv * 4 + 4;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(base) + size_t(key0) * hkv, (short)0, left > 0 ? left : 0, kRsrcWord3);
+#pragma unroll
+        for (int i = 0; i < C::NRK; ++i)
+          buf[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, sc_off[i], 0, kCpolNT));
       }
     };
 
     // Tile j: K in kb (two register stages, the next K tile always in flight),
     // V in vb (one stage: the next V tile is issued as soon as this one is in LDS).
     // k_next / v_next: tiles to issue into kb / vb once they are consumed (-1: none).
-    auto process = [&](int j, u32x4_t* kb, u32x4_t* vb, int k_next, int v_next) {
+    auto process = [&](int j, Raw* kb, float* ksb, Raw* vb, float* vsb, int k_next, int v_next) {
       // ---- partial dots of slot s against the GB queries, then the head-splitting
       // steps of the transpose-reduction (independent per slot, so each slot is
       // reduced as soon as its dots are formed).
@@ -287,12 +351,13 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
 #pragma unroll
       for (int s = 0; s < C::NR; ++s) {
         float r8[GB];
+        const u32x4_t kw = E::widen(kb[s]);
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
-          float a = dot2_bf16(q[h].x, kb[s].x, 0.f);
-          a = dot2_bf16(q[h].y, kb[s].y, a);
-          a = dot2_bf16(q[h].z, kb[s].z, a);
-          r8[h] = dot2_bf16(q[h].w, kb[s].w, a);
+          float a = dot2_bf16(q[h].x, kw.x, 0.f);
+          a = dot2_bf16(q[h].y, kw.y, a);
+          a = dot2_bf16(q[h].z, kw.z, a);
+          r8[h] = dot2_bf16(q[h].w, kw.w, a);
         }
 #define KVC_HSTEP(K)                                                         \
   if constexpr (K < C::HB) {                                                 \
@@ -306,7 +371,13 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
 #undef KVC_HSTEP
         R[s][0] = r8[0];
       }
-      if (k_next >= 0) issue(kseg, k_next, kb);  // this K stage is free again
+      float ks[C::NRK];  // this tile's K scales, taken before the stage is reused
+#pragma unroll
+      for (int r = 0; r < C::NRK; ++r) ks[r] = Q8 ? ksb[r] : 1.f;
+      if (k_next >= 0) {  // this K stage is free again
+        issue(kseg, k_next, kb);
+        issue_sc(ksseg, k_next, ksb);
+      }
       // ---- row-splitting steps: the lane keeps the half of its slots its index bit selects
       int off = 0;
 #define KVC_RSTEP(K)                                                         \
@@ -330,7 +401,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
       for (int r = 0; r < C::NRK; ++r) {
         const int slot = r + off;
         const int row = 2 * ((slot >> 1) * C::RPI + rg) + (slot & 1);
-        y[r] = key0 + row < L ? R[r][0] * c : -INFINITY;
+        y[r] = key0 + row < L ? R[r][0] * (Q8 ? c * ks[r] : c) : -INFINITY;
       }
       bool raise = false;
 #pragma unroll
@@ -366,12 +437,15 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
 #pragma unroll
       for (int jp = 0; jp < C::NPK; ++jp) {
         const int pair = ((2 * jp + off) >> 1) * C::RPI + rg;
-        plds[pair * GB + ghx] = pack_bf16x2(pr[2 * jp], pr[2 * jp + 1]);
+        if constexpr (Q8)
+          plds[pair * GB + ghx] = pack_bf16x2(pr[2 * jp] * vsb[2 * jp], pr[2 * jp + 1] * vsb[2 * jp + 1]);
+        else
+          plds[pair * GB + ghx] = pack_bf16x2(pr[2 * jp], pr[2 * jp + 1]);
       }
 #pragma unroll
       for (int sp = 0; sp < C::NR / 2; ++sp) {
         const int pair = sp * C::RPI + rg;
-        const u32x4_t v0 = vb[2 * sp], v1 = vb[2 * sp + 1];
+        const u32x4_t v0 = E::widen(vb[2 * sp]), v1 = E::widen(vb[2 * sp + 1]);
         uint4 a, b;
         a.x = pack_lo16(v0.x, v1.x); a.y = pack_hi16(v0.x, v1.x);
         a.z = pack_lo16(v0.y, v1.y); a.w = pack_hi16(v0.y, v1.y);
@@ -381,7 +455,10 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
         dst[0] = a;
         dst[1] = b;
       }
-      if (v_next >= 0) issue(vseg, v_next, vb);
+      if (v_next >= 0) {
+        issue(vseg, v_next, vb);
+        issue_sc(vsseg, v_next, vsb);
+      }
       wave_lds_fence();
       // ---- P*V: lane owns dims [DL*lane, DL*lane + DL) of all GB heads
 #pragma unroll 4
@@ -408,19 +485,25 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
     };
 
     // The wave's tiles of this run: j0 + wave, j0 + wave + 4, ...
-    u32x4_t kA[C::NR], kB[C::NR], vb[C::NR];
+    Raw kA[C::NR], kB[C::NR], vb[C::NR];
+    float ksA[C::NRK], ksB[C::NRK], vsb[C::NRK];
     int j = j0 + wave;
     if (j < j1) {
       issue(kseg, j, kA);
+      issue_sc(ksseg, j, ksA);
       issue(vseg, j, vb);
-      if (j + kWaves < j1) issue(kseg, j + kWaves, kB);
+      issue_sc(vsseg, j, vsb);
+      if (j + kWaves < j1) {
+        issue(kseg, j + kWaves, kB);
+        issue_sc(ksseg, j + kWaves, ksB);
+      }
     }
     auto next = [&](int jj) { return jj < j1 ? jj : -1; };
     while (j < j1) {
-      process(j, kA, vb, next(j + 2 * kWaves), next(j + kWaves));
+      process(j, kA, ksA, vb, vsb, next(j + 2 * kWaves), next(j + kWaves));
       j += kWaves;
       if (j >= j1) break;
-      process(j, kB, vb, next(j + 2 * kWaves), next(j + kWaves));
+      process(j, kB, ksB, vb, vsb, next(j + 2 * kWaves), next(j + kWaves));
       j += kWaves;
     }
 
@@ -578,7 +661,10 @@ __global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p
 
 template <int D, int GB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_bf16_kernel<D, GB>), dim3(p.n_wg), dim3(kWaves * kWave), 0, s, p);
+  if (p.kv.dtype == KVC_I8)
+    hipLaunchKernelGGL((decode_bf16_kernel<D, GB, true>), dim3(p.n_wg), dim3(kWaves * kWave), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_bf16_kernel<D, GB, false>), dim3(p.n_wg), dim3(kWaves * kWave), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long n_comb = (long long)p.kv.batch * p.kv.n_kv_heads * p.n_hb * GB;

@@ -17,7 +17,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_cache(const kvc_cache* c) {
   if (!c || !c->k || !c->v || !c->seqlens) return KVC_E_ARG;
   if (!aligned16(c->k) || !aligned16(c->v) || (reinterpret_cast<uintptr_t>(c->seqlens) & 3u)) return KVC_E_ARG;
-  if (c->dtype != KVC_F32 && c->dtype != KVC_BF16) return KVC_E_DTYPE;
+  if (c->dtype != KVC_F32 && c->dtype != KVC_BF16 && c->dtype != KVC_I8) return KVC_E_DTYPE;
+  if (c->dtype == KVC_I8 && (!c->k_scale || !c->v_scale || (reinterpret_cast<uintptr_t>(c->k_scale) & 3u) ||
+                             (reinterpret_cast<uintptr_t>(c->v_scale) & 3u)))
+    return KVC_E_ARG;
   if (c->n_layers < 1 || c->batch < 1 || c->max_seq < 1 || c->n_kv_heads < 1) return KVC_E_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return KVC_E_SHAPE;
   return KVC_OK;
@@ -28,9 +31,12 @@ int check_heads(const kvc_cache* c, int32_t n_q_heads) {
   return KVC_OK;
 }
 
+size_t elem_bytes(int32_t dtype) { return dtype == KVC_F32 ? 4 : dtype == KVC_BF16 ? 2 : 1; }
+
 kvc::LayerView layer_view(const kvc_cache* c, int32_t layer) {
-  const size_t esz = c->dtype == KVC_BF16 ? 2 : 4;
-  const size_t layer_bytes = size_t(c->batch) * c->max_seq * c->n_kv_heads * c->head_dim * esz;
+  const size_t esz = elem_bytes(c->dtype);
+  const size_t layer_vecs = size_t(c->batch) * c->max_seq * c->n_kv_heads;
+  const size_t layer_bytes = layer_vecs * c->head_dim * esz;
   kvc::LayerView v;
   v.k = static_cast<uint8_t*>(c->k) + size_t(layer) * layer_bytes;
   v.v = static_cast<uint8_t*>(c->v) + size_t(layer) * layer_bytes;
@@ -40,6 +46,8 @@ kvc::LayerView layer_view(const kvc_cache* c, int32_t layer) {
   v.n_kv_heads = c->n_kv_heads;
   v.head_dim = c->head_dim;
   v.dtype = c->dtype;
+  v.k_scale = c->dtype == KVC_I8 ? c->k_scale + size_t(layer) * layer_vecs : nullptr;
+  v.v_scale = c->dtype == KVC_I8 ? c->v_scale + size_t(layer) * layer_vecs : nullptr;
   return v;
 }
 
@@ -83,7 +91,7 @@ DecodePlan decode_plan(const kvc_cache* c, int32_t n_q_heads, int32_t n_workers)
 }
 
 size_t decode_ws_bytes(const kvc_cache* c, int32_t n_q_heads, int32_t n_workers) {
-  if (c->dtype == KVC_BF16) {
+  if (c->dtype != KVC_F32) {  // bfloat16 and int8 caches share the split-KV plan
     const DecodePlan pl = decode_plan(c, n_q_heads, n_workers);
     if (pl.n_wg <= 0) return 0;
     return size_t(pl.n_wg) * 2 * size_t(pl.gb) * size_t(c->head_dim + 2) * sizeof(float);
@@ -122,6 +130,7 @@ int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* 
   for (int i = 0; i < 64; ++i)
     p.inv_freq[i] = i < cache->head_dim / 2 ? float(pow(double(rope_base), -2.0 * i / cache->head_dim)) : 0.f;
   p.dev_err = dev_err;
+  if (cache->dtype == KVC_I8) return launch_status(kvc::launch_rope_append_q8(p, static_cast<hipStream_t>(stream)));
   return launch_status(kvc::launch_rope_append(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -145,12 +154,12 @@ int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, vo
   const size_t need = decode_ws_bytes(cache, n_q_heads, n_workers);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return KVC_E_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (cache->dtype == KVC_BF16) {
+  if (cache->dtype != KVC_F32) {  // bfloat16 or int8 cache
     const DecodePlan pl = decode_plan(cache, n_q_heads, n_workers);
     if (pl.n_wg <= 0) return KVC_E_LAUNCH;
     // Flattened tile indices and in-row byte offsets are 32-bit.
     const int64_t tiles = int64_t(cache->batch) * cache->n_kv_heads * pl.n_hb * ((int64_t(cache->max_seq) + 31) / 32);
-    const int64_t row_span = int64_t(cache->max_seq) * cache->n_kv_heads * cache->head_dim * 2;
+    const int64_t row_span = int64_t(cache->max_seq) * cache->n_kv_heads * cache->head_dim * 2;  // bfloat16 bound
     if (tiles >= (int64_t(1) << 31) || row_span >= (int64_t(1) << 31)) return KVC_E_SHAPE;
     if (int64_t(cache->batch) * cache->n_kv_heads * pl.n_hb * pl.gb > 0x7fffffffLL) return KVC_E_SHAPE;
     kvc::DecodeParams p;
@@ -196,6 +205,7 @@ int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, v
   if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
   float sc;
   if (!resolve_scale(scale, cache->head_dim, &sc)) return KVC_E_ARG;
+  if (cache->dtype == KVC_I8) return KVC_E_DTYPE;  // prefill reads bfloat16 or float32 caches
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->dtype == KVC_BF16) {
     // The kernel's buffer descriptors span one head row with 32-bit byte offsets.
@@ -231,6 +241,7 @@ int kvc_decode_step(const kvc_cache* cache, int32_t layer, const void* q, const 
                     void* out, int32_t n_q_heads, float scale, float rope_base, int32_t* dev_err, void* stream) {
   int st = check_cache(cache);
   if (st != KVC_OK) return st;
+  if (cache->dtype == KVC_I8) return KVC_E_DTYPE;  // the fused step keeps float32 / bfloat16 caches
   if (layer < 0 || layer >= cache->n_layers) return KVC_E_ARG;
   if (!q || !k_new || !v_new || !out) return KVC_E_ARG;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return KVC_E_ARG;

@@ -15,6 +15,8 @@ struct LayerView {
   void* v;
   const int32_t* seqlens;
   int32_t batch, max_seq, n_kv_heads, head_dim, dtype;
+  float* k_scale;  // int8 caches: (batch, max_seq, n_kv_heads) scales of this layer; else null
+  float* v_scale;
 };
 
 struct RopeAppendParams {
@@ -28,6 +30,8 @@ struct RopeAppendParams {
   int32_t* dev_err;
 };
 hipError_t launch_rope_append(const RopeAppendParams& p, hipStream_t s);
+// Same call on an int8 cache: q/q_out/k_new/v_new bfloat16, K/V quantized per vector.
+hipError_t launch_rope_append_q8(const RopeAppendParams& p, hipStream_t s);
 
 // Split-KV attention over rows (b, t): row b's query t attends to keys 0..seqlens[b]+t.
 // Decode is T = 1.  With one split per row ("direct") the output is written

@@ -101,6 +101,97 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendParams p) {
   for (int it = threadIdx.x; it < n_vec; it += blockDim.x) v_dst[it] = v_src[it];
 }
 
+// int8 cache (Cake paper, Section 5.1 "Compression methods", Section 5.5):
+// the queries are rotated into q_out (bfloat16) exactly as above; each new
+// key -- rotated with the same pair rotation and rounded to bfloat16, the
+// value a bfloat16 cache would hold -- and each value vector is quantized per
+// (token, KV head): s = amax / 127 in float32, codes round_half_even(x / s)
+// in [-127, 127] (float32 quotient), s = 0 and codes 0 for an all-zero
+// vector.  One wave per vector: a lane holds head_dim / 64 of its elements.
+template <int D>
+__global__ __launch_bounds__(256) void rope_append_q8_kernel(RopeAppendParams p) {
+  constexpr int HALF = D / 2;
+  constexpr int QUADS = HALF / 4;
+  constexpr int EPL = D / kWave;  // elements per lane
+  __shared__ __align__(16) float cs[HALF];
+  __shared__ __align__(16) float sn[HALF];
+
+  const int row = blockIdx.x;  // b * T + t
+  const int b = row / p.T;
+  const int t = row - b * p.T;
+  const int start = p.kv.seqlens[b];
+  if (start < 0 || start > p.kv.max_seq - p.T) {
+    if (t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
+    return;
+  }
+  const int pos = start + t;
+  if (threadIdx.x < HALF) {
+    const float theta = __fmul_rn(static_cast<float>(pos), p.inv_freq[threadIdx.x]);
+    float s, c;
+    sincosf(theta, &s, &c);
+    cs[threadIdx.x] = c;
+    sn[threadIdx.x] = s;
+  }
+  __syncthreads();
+
+  const int hq = p.n_q_heads;
+  const int hkv = p.kv.n_kv_heads;
+  const bf16_t* q_row = static_cast<const bf16_t*>(p.q) + size_t(row) * hq * D;
+  bf16_t* q_out_row = static_cast<bf16_t*>(p.q_out) + size_t(row) * hq * D;
+  for (int it = threadIdx.x; it < hq * QUADS; it += blockDim.x) {
+    const int head = it / QUADS;
+    const int i0 = (it - head * QUADS) * 4;
+    float a[4], b2[4], ra[4], rb[4];
+    Vec4<bf16_t>::load(q_row + head * D + i0, a);
+    Vec4<bf16_t>::load(q_row + head * D + i0 + HALF, b2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rope_pair(a[j], b2[j], cs[i0 + j], sn[i0 + j], ra[j], rb[j]);
+    Vec4<bf16_t>::store(q_out_row + head * D + i0, ra);
+    Vec4<bf16_t>::store(q_out_row + head * D + i0 + HALF, rb);
+  }
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const size_t vec0 = (size_t(b) * p.kv.max_seq + pos) * hkv;  // this position's first (head) vector
+  for (int vi = wave; vi < 2 * hkv; vi += blockDim.x / kWave) {
+    const bool is_k = vi < hkv;
+    const int g = is_k ? vi : vi - hkv;
+    const bf16_t* src = static_cast<const bf16_t*>(is_k ? p.k_new : p.v_new) + (size_t(row) * hkv + g) * D;
+    float x[EPL];
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) {
+      const int e = lane + kWave * u;
+      if (is_k) {
+        const int i = e < HALF ? e : e - HALF;
+        float xr, yr;
+        rope_pair(bf16_to_f32(src[i]), bf16_to_f32(src[i + HALF]), cs[i], sn[i], xr, yr);
+        x[u] = bf16_to_f32(f32_to_bf16(e < HALF ? xr : yr));
+      } else {
+        x[u] = bf16_to_f32(src[e]);
+      }
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) am = fmaxf(am, fabsf(x[u]));
+    am = wave_max(am);
+    const float sc = am / 127.f;
+    int8_t* dst = static_cast<int8_t*>(is_k ? p.kv.k : p.kv.v) + (vec0 + g) * D;
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) {
+      const float c = sc > 0.f ? fminf(fmaxf(rintf(x[u] / sc), -127.f), 127.f) : 0.f;
+      dst[lane + kWave * u] = static_cast<int8_t>(c);
+    }
+    if (lane == 0) (is_k ? p.kv.k_scale : p.kv.v_scale)[vec0 + g] = sc;
+  }
+}
+
+hipError_t launch_rope_append_q8(const RopeAppendParams& p, hipStream_t s) {
+  const dim3 grid(p.kv.batch * p.T), block(256);
+  if (p.kv.head_dim == 128) hipLaunchKernelGGL((rope_append_q8_kernel<128>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((rope_append_q8_kernel<64>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_append(const RopeAppendParams& p, hipStream_t s) {
   const dim3 grid(p.kv.batch * p.T);
   const dim3 block(256);

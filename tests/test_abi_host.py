@@ -158,3 +158,26 @@ def test_decode_step_validation(lib):
     assert call(d, 0, q, q, q, q, 4 * 17, 0.0, 1e4, None, None) == lib.KVC_E_SHAPE  # group of 17 > 16
     assert call(_desc(lib, head_dim=96), 0, *ok) == lib.KVC_E_SHAPE
     assert call(_desc(lib, dtype=7), 0, *ok) == lib.KVC_E_DTYPE
+
+
+def test_int8_cache_validation(lib):
+    L = lib.lib
+    q = P(0x40000)
+    no_scales = _desc(lib, dtype=lib.KVC_I8)
+    assert L.kvc_attn_decode(ctypes.byref(no_scales), 0, q, q, 16, 0.0, 0, P(0x70000), 1 << 30, None,
+                             None) == lib.KVC_E_ARG  # an int8 cache needs both scale arrays
+    d = _desc(lib, dtype=lib.KVC_I8)
+    d.k_scale, d.v_scale = 0x50000, 0x60000
+    bad = _desc(lib, dtype=lib.KVC_I8)
+    bad.k_scale, bad.v_scale = 0x50002, 0x60000  # misaligned scale array
+    assert L.kvc_rope_append(ctypes.byref(bad), 0, q, q, q, q, 1, 16, 1e4, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_prefill(ctypes.byref(d), 0, q, q, 4, 16, 0.0, None, None) == lib.KVC_E_DTYPE
+    assert L.kvc_decode_step(ctypes.byref(d), 0, q, q, q, q, 16, 0.0, 1e4, None, None) == lib.KVC_E_DTYPE
+    # the int8 decode shares the bfloat16 plan and workspace
+    bf = _desc(lib)
+    W = L.kvc_decode_workspace_bytes
+    assert W(ctypes.byref(d), 16, 10) == W(ctypes.byref(bf), 16, 10) > 0
+    src = _desc(lib, batch=1, dtype=lib.KVC_I8)
+    src.k_scale, src.v_scale = 0x50000, 0x60000
+    assert L.kvc_prefill_clone(ctypes.byref(src), 10, ctypes.byref(_desc(lib, batch=8)), None,
+                               None) == lib.KVC_E_DTYPE  # int8 source, bfloat16 destination
