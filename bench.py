@@ -17,6 +17,11 @@ oracle timed on a bounded sample of the same work.
 
     python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
 
+`--workload long_context_int8` runs the same decode steps on an int8 cache
+(codes plus one float32 scale per cached vector): the 72K context is written
+by the quantizing append alone (prefill attention reads bfloat16 caches
+only), then cloned and decoded as above.
+
 `--workload tiny` instead times the two tiny fp32 workloads' decode steps
 (one attention layer at batch 1; the six-layer tiny GPT at batch 16), which
 are bound by kernel launches: per step through kvc_rope_append +
@@ -69,7 +74,7 @@ def measured_traffic(name: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=["long_context", "tiny"], default="long_context")
+    ap.add_argument("--workload", choices=["long_context", "long_context_int8", "tiny"], default="long_context")
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps per batch size (default 512)")
@@ -114,6 +119,8 @@ def main():
         sys.exit(2)
     if args.workload == "tiny":
         return bench_tiny(args)
+    if args.workload == "long_context_int8":
+        return bench_int8(args)
     import kv_cache_attention_kvcache_amd as kvc
     import synth
 
@@ -257,6 +264,84 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, kv_bytes_tok, q_)
     print(json.dumps(res), flush=True)
+
+
+def bench_int8(args):
+    """Decode on an int8 cache at the long-context workload's shapes; one JSON line."""
+    import kv_cache_attention_kvcache_amd as kvc
+    import synth
+
+    w = synth.LONG_CONTEXT
+    ctx, chunk = w.extra["context"], w.extra["chunk"]
+    n_dec = w.extra["steps"] if args.decode_steps is None else args.decode_steps
+    rows, hq, hkv, d, max_seq = w.extra["clone_rows"], w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_seq
+    bf = torch.bfloat16
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(bf).to(dev)
+    chunks = [tuple(to_dev(a[None]) for a in synth.chunk_qkv(w, c, chunk)) for c in range(ctx // chunk)]
+    dec = {1: [], rows: []}
+    for s_ in range(n_dec):
+        q, k, v = synth.decode_qkv_batch(w, s_, rows)
+        for b in (1, rows):
+            dec[b].append((to_dev(q[:b]), to_dev(k[:b]), to_dev(v[:b])))
+    cache1 = kvc.KVCache.empty(1, 1, max_seq, hkv, d, dtype=torch.int8, device=dev)
+    cache8 = kvc.KVCache.empty(1, rows, max_seq, hkv, d, dtype=torch.int8, device=dev)
+    ws = torch.zeros(kvc.kvc_decode_workspace_bytes(cache8, hq), dtype=torch.uint8, device=dev)
+    qrot = {b: torch.empty((b, 1, hq, d), dtype=bf, device=dev) for b in (1, rows)}
+    out = {b: torch.empty((b, 1, hq, d), dtype=bf, device=dev) for b in (1, rows)}
+    qrot_p = torch.empty((1, chunk, hq, d), dtype=bf, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    t_dec = {1: Timer(), rows: Timer()}
+
+    def step(timed):
+        cache1.seqlens.zero_()
+        cache8.seqlens.zero_()
+        for q, k, v in chunks:
+            kvc.kvc_rope_append(cache1, 0, q, k, v, q_out=qrot_p, dev_err=err)
+            cache1.seqlens += chunk
+        kvc.kvc_prefill_clone(cache1, ctx, cache8, dev_err=err)
+        for b, cache in ((1, cache1), (rows, cache8)):
+            for s_ in range(n_dec):
+                q, k, v = dec[b][s_]
+                kvc.kvc_rope_append(cache, 0, q, k, v, q_out=qrot[b], dev_err=err)
+                with t_dec[b] if timed else _Null():
+                    kvc.kvc_attn_decode(cache, 0, qrot[b], out=out[b], workspace=ws, dev_err=err)
+                cache.seqlens += 1
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.time()
+    for i in range(K):
+        step(True)
+        log(f"timed step {i} enqueued", args.quiet)
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    assert err.item() == 0, f"device error bits {err.item()}"
+    vec_bytes = 2 * hkv * (d + 4)  # K and V codes plus their float32 scales, per token
+    dec_bytes = {b: b * sum((ctx + s_ + 1) * vec_bytes for s_ in range(n_dec)) for b in (1, rows)}
+    ms = {b: sum(t_dec[b].times_ms()) for b in (1, rows)}
+    gbps = {b: K * dec_bytes[b] / (ms[b] * 1e-3) / 1e9 for b in (1, rows)}
+    total = K * (dec_bytes[1] + dec_bytes[rows]) / ((ms[1] + ms[rows]) * 1e-3) / 1e9
+    per_launch = dec_bytes[rows] / n_dec
+    avg_ms = ms[rows] / (K * n_dec)
+    print(json.dumps({
+        "metric": "KV-cache decode attn HBM GB/s on an int8 cache (codes + scales)", "value": round(total, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": w.name + "_int8_decode", "context": ctx, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": d, "decode_steps": n_dec, "decode_batches": [1, rows], "parallelism": "none"},
+        "decode_gbps_by_batch": {str(b): round(gbps[b], 1) for b in (1, rows)},
+        "decode_us_by_batch": {str(b): round(ms[b] * 1e3 / (K * n_dec), 2) for b in (1, rows)},
+        "decode_tokens_per_s_by_batch": {str(b): round(b * K * n_dec / (ms[b] * 1e-3), 1) for b in (1, rows)},
+        "roofline": {"bound": "hbm", "kernel": "decode_bf16_kernel<int8> + decode_bf16_combine_kernel, batch 8",
+                     "achieved": round(per_launch / (avg_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(per_launch / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "note": "vector-ALU bound: widening the codes and the 2 x 8 GQA products per cached "
+                             "element pair exceed the ALU budget per HBM byte at int8"}}), flush=True)
 
 
 class _TinyModel:
