@@ -572,6 +572,311 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
   }
 }
 
+// ---------------------------------------------------------------------------
+// int8 caches on matrix cores.
+//
+// At a GQA group of 8, widening the int8 codes and forming the 2 x 8 products
+// of every cached element pair on vector ALUs costs more ALU time per HBM
+// byte than the chip has (that path streams about 1.6 TB/s).  Here the
+// products run on MFMA (v_mfma_f32_32x32x16_bf16) and the vector ALUs only
+// widen codes and run the softmax.  A segment is (row, KV head) with all its
+// query heads (G <= 32) as the 32 columns of the MFMA B operand; the tile
+// partition, the per-run fold of the four waves and the partials are those of
+// decode_bf16_kernel with a 32-head block.
+//
+// One 32-key tile, per wave:
+//   * S^T = K Q^T.  Lane (A row i, half h) holds the key of tile row
+//     perm_key(i): the order that leaves each lane with two 8-key runs of its
+//     head's scores, which is the B operand P*V needs.  The head-dim axis of
+//     the contraction is permuted the same way for K and for Q: at k-step
+//     2m + e a lane's 8 elements are head dims 32m + 16h + 8e .. +8, so each
+//     16-byte load of 16 codes gives the lane two k-steps.  Codes widen to
+//     bfloat16 exactly (|code| <= 127).
+//   * The tile's 32 K scales and 32 V scales go through wave-private LDS (one
+//     load per lane).  A key's K scale multiplies its scores, its V scale the
+//     probability that weights its codes in P*V; the softmax sum takes the
+//     unscaled probability.  Lazy running max per head as in the vector path.
+//   * V^T in LDS as bfloat16 key pairs per head dim; O^T += V^T P^T.
+constexpr int kQ8Cols = 32;  // query heads per segment (MFMA columns)
+
+// Tile row fed as A-operand row i so that output register r of lane (column,
+// half h) holds key 16 (r >> 3) + 8 h + (r & 7).
+__device__ __forceinline__ int perm_key(int i) {
+  return ((i >> 4) << 4) | (((i >> 2) & 1) << 3) | (((i >> 3) & 1) << 2) | (i & 3);
+}
+
+__device__ __forceinline__ uint32_t i8_pair_bf16(uint32_t w, int byte) {
+  return pack_bf16x2(static_cast<float>(static_cast<int8_t>(w >> (8 * byte))),
+                     static_cast<float>(static_cast<int8_t>(w >> (8 * byte + 8))));
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * kWave, 1) void decode_q8_mfma_kernel(DecodeParams p) {
+  constexpr int GB = kQ8Cols;
+  constexpr int kM = D / 32;                      // 16-byte K loads per lane per tile
+  constexpr int kKD = D / 16;                     // MFMA k-steps of S^T
+  constexpr int kDB = D / 32;                     // 32-dim blocks of O^T
+  constexpr int kVItems = 16 * (D / 8) / kWave;   // (key pair, 8-dim group) items per lane
+  constexpr int kVStride = 80;                    // bytes per head-dim row of V^T: 16 key pairs + pad
+  constexpr int kWaveLds = D * kVStride + 64 * 4;
+  constexpr int kMerge = kWaves * GB * (D + 2) * 4;
+  constexpr int kLds = kWaves * kWaveLds > kMerge ? kWaves * kWaveLds : kMerge;
+  __shared__ __align__(16) uint8_t smem[kLds];
+
+  const int wave = uniform(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  const int n_tiles = total_tiles(p, lane);
+  const int t_begin = range_begin(blockIdx.x, n_tiles, p.n_wg);
+  const int t_end = range_begin(blockIdx.x + 1LL, n_tiles, p.n_wg);
+  if (t_begin >= t_end) return;
+
+  const int hq = p.n_q_heads;
+  const int hkv = p.kv.n_kv_heads;
+  const int group = hq / hkv;
+  const int spr = hkv;  // one 32-head block per KV head
+  const int row_bytes = hkv * D;
+  const float c = p.scale_log2;
+  const int key_a = perm_key(l32);  // this lane's A-operand key within a tile
+
+  uint8_t* vt = smem + wave * kWaveLds;                           // V^T of the wave's tile
+  float* scl = reinterpret_cast<float*>(vt + D * kVStride);       // [0,32) K scales, [32,64) V scales
+
+  SegPos seg = find_segment(p, t_begin, lane);
+  int t = t_begin;
+  bool first_run = true;
+  while (t < t_end) {
+    const int seg_end = seg.base + seg.nt;
+    const int run_end = min(t_end, seg_end);
+    const bool complete = t == seg.base && run_end == seg_end;
+    const int g = seg.sr;
+    const int L = p.kv.seqlens[seg.b] + 1;
+    const int j0 = t - seg.base, j1 = run_end - seg.base;
+
+    const size_t vec0 = size_t(seg.b) * p.kv.max_seq * hkv + g;
+    const uint8_t* kseg = static_cast<const uint8_t*>(p.kv.k) + vec0 * D;
+    const uint8_t* vseg = static_cast<const uint8_t*>(p.kv.v) + vec0 * D;
+    const float* ksseg = p.kv.k_scale + vec0;
+    const float* vsseg = p.kv.v_scale + vec0;
+
+    // Q^T B operands: lane (column = query head l32 of the group, half): head
+    // dims 32m + 16 half + 8e .. +8 at k-step 2m + e; zero for padding heads.
+    u32x4_t qb[kKD];
+    {
+      const bool valid = l32 < group;
+      const bf16_t* qrow = static_cast<const bf16_t*>(p.q) + (size_t(seg.b) * hq + g * group + (valid ? l32 : 0)) * D;
+#pragma unroll
+      for (int m = 0; m < kM; ++m)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          qb[2 * m + e] = valid ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * m + 16 * half + 8 * e)
+                                : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    f32x16_t o[kDB];
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    float mh = -INFINITY, lpart = 0.f;  // head l32's running max (log2 units) and this lane's share of its sum
+
+    auto rsrc_at = [&](const void* base, int j, int unit, int per_key) {
+      const int key0 = j * kTileKeys;
+      const int left = (L - key0 - 1) * per_key + unit;  // valid bytes from the tile's first key
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(base)) +
+                                                   size_t(key0) * per_key,
+                                               (short)0, left > 0 ? left : 0, kRsrcWord3);
+    };
+    struct Stage {
+      u32x4_t k[kM];
+      u32x2_t v[kVItems][2];
+      float ks, vs;
+    };
+    auto issue = [&](int j, Stage& st) {
+      const __amdgpu_buffer_rsrc_t rk = rsrc_at(kseg, j, D, row_bytes);
+      const __amdgpu_buffer_rsrc_t rv = rsrc_at(vseg, j, D, row_bytes);
+      // Each load takes part of a row (other loads of this wave take the rest), so the
+      // lines must stay cached between them: no streaming hint here.
+#pragma unroll
+      for (int m = 0; m < kM; ++m)
+        st.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, key_a * row_bytes + 32 * m + 16 * half, 0, 0);
+#pragma unroll
+      for (int it = 0; it < kVItems; ++it) {
+        const int i = lane + kWave * it;
+        const int kp = i & 15, dg = i >> 4;
+        st.v[it][0] = __builtin_amdgcn_raw_buffer_load_b64(rv, 2 * kp * row_bytes + 8 * dg, 0, 0);
+        st.v[it][1] = __builtin_amdgcn_raw_buffer_load_b64(rv, (2 * kp + 1) * row_bytes + 8 * dg, 0, 0);
+      }
+      const __amdgpu_buffer_rsrc_t rks = rsrc_at(ksseg, j, 4, hkv * 4);
+      const __amdgpu_buffer_rsrc_t rvs = rsrc_at(vsseg, j, 4, hkv * 4);
+      st.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, l32 * hkv * 4, 0, kCpolNT));
+      st.vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, l32 * hkv * 4, 0, kCpolNT));
+    };
+    auto process = [&](int j, Stage& st, int j_next) {
+      // ---- V^T key pairs and the scales into the wave's LDS (the last tile's reads are done)
+      wave_lds_fence();
+#pragma unroll
+      for (int it = 0; it < kVItems; ++it) {
+        const int i = lane + kWave * it;
+        const int kp = i & 15, dg = i >> 4;
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const uint32_t wa = dd < 4 ? st.v[it][0].x : st.v[it][0].y;
+          const uint32_t wb = dd < 4 ? st.v[it][1].x : st.v[it][1].y;
+          const int sh = 8 * (dd & 3);
+          *reinterpret_cast<uint32_t*>(vt + (8 * dg + dd) * kVStride + 4 * kp) =
+              pack_bf16x2(static_cast<float>(static_cast<int8_t>(wa >> sh)),
+                          static_cast<float>(static_cast<int8_t>(wb >> sh)));
+        }
+      }
+      scl[lane] = half ? st.vs : st.ks;  // K scale of key l32, or V scale of key l32
+      // ---- K A operands from this stage; then the stage takes tile j_next
+      u32x4_t ka[kKD];
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        const u32x4_t w = st.k[m];
+        ka[2 * m] = u32x4_t{i8_pair_bf16(w.x, 0), i8_pair_bf16(w.x, 2), i8_pair_bf16(w.y, 0), i8_pair_bf16(w.y, 2)};
+        ka[2 * m + 1] = u32x4_t{i8_pair_bf16(w.z, 0), i8_pair_bf16(w.z, 2), i8_pair_bf16(w.w, 0), i8_pair_bf16(w.w, 2)};
+      }
+      const float ks_l = st.ks, vs_l = st.vs;
+      (void)ks_l;
+      (void)vs_l;
+      if (j_next >= 0) issue(j_next, st);
+      // ---- S^T = K Q^T
+      f32x16_t s;
+#pragma unroll
+      for (int kd = 0; kd < kKD; ++kd)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[kd]),
+                                                    __builtin_bit_cast(bf16x8_t, qb[kd]),
+                                                    kd == 0 ? f32x16_t{} : s, 0, 0, 0);
+      wave_lds_fence();  // V^T and the scales are visible to the whole wave
+      // ---- softmax of head l32 over this lane's 16 keys: key(r) = 16 (r >> 3) + 8 half + (r & 7)
+      const int key0 = j * kTileKeys;
+      float ks[16], vs[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int k4 = 16 * (q4 >> 1) + 8 * half + 4 * (q4 & 1);
+        const float4 a = *reinterpret_cast<const float4*>(scl + k4);
+        const float4 b = *reinterpret_cast<const float4*>(scl + 32 + k4);
+        ks[4 * q4] = a.x; ks[4 * q4 + 1] = a.y; ks[4 * q4 + 2] = a.z; ks[4 * q4 + 3] = a.w;
+        vs[4 * q4] = b.x; vs[4 * q4 + 1] = b.y; vs[4 * q4 + 2] = b.z; vs[4 * q4 + 3] = b.w;
+      }
+      float y[16];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 16 * (r >> 3) + 8 * half + (r & 7);
+        y[r] = key < L ? s[r] * (c * ks[r]) : -INFINITY;
+        tm = fmaxf(tm, y[r]);
+      }
+      tm = fmaxf(tm, __shfl_xor(tm, 32));  // the head's max over the tile (both halves)
+      if (__ballot(tm > mh + kLazyLog2)) {
+        const float m_new = fmaxf(mh, tm);  // finite: key key0 is always valid
+        const float alpha = exp2f(mh - m_new);
+        mh = m_new;
+        lpart *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      u32x4_t pf[2];
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * ks2 + 2 * i;
+          const float p0 = exp2f(y[r] - mh), p1 = exp2f(y[r + 1] - mh);
+          lpart += p0 + p1;
+          w[i] = pack_bf16x2(p0 * vs[r], p1 * vs[r + 1]);
+        }
+        pf[ks2] = u32x4_t{w[0], w[1], w[2], w[3]};
+      }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vt + (32 * db + l32) * kVStride + (8 * ks2 + 4 * half) * 4);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          __builtin_bit_cast(bf16x8_t, pf[ks2]), o[db], 0, 0, 0);
+        }
+    };
+
+    // The wave's tiles of this run: j0 + wave, j0 + wave + 4, ...; two stages in flight.
+    Stage sa, sb;
+    int j = j0 + wave;
+    if (j < j1) issue(j, sa);
+    if (j + kWaves < j1) issue(j + kWaves, sb);
+    auto next = [&](int jj) { return jj < j1 ? jj : -1; };
+    while (j < j1) {
+      process(j, sa, next(j + 2 * kWaves));
+      j += kWaves;
+      if (j >= j1) break;
+      process(j, sb, next(j + 2 * kWaves));
+      j += kWaves;
+    }
+
+    // ---- fold the four waves' states of this run (as decode_bf16_kernel, 32 heads)
+    lpart += __shfl_xor(lpart, 32);
+    __syncthreads();
+    float* red_ml = reinterpret_cast<float*>(smem);   // [wave][GB][2]
+    float* red_o = red_ml + kWaves * GB * 2;          // [wave][GB][D]
+    if (half == 0) {
+      red_ml[(wave * GB + l32) * 2] = mh;
+      red_ml[(wave * GB + l32) * 2 + 1] = lpart;
+    }
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(red_o + (wave * GB + l32) * D + 32 * db + 8 * r4 + 4 * half) =
+            make_float4(o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]);
+    __syncthreads();
+    const int slot = first_run ? 0 : 1;
+    for (int e = threadIdx.x; e < group * D && e < GB * D; e += kWaves * kWave) {
+      const int h = e / D;
+      const int d = e - h * D;
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, red_ml[(w * GB + h) * 2]);
+      float ov = 0.f, l = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2f(red_ml[(w * GB + h) * 2] - mm);  // 0 for a wave with no tile here
+        ov += f * red_o[(w * GB + h) * D + d];
+        l += f * red_ml[(w * GB + h) * 2 + 1];
+      }
+      if (complete) {
+        static_cast<bf16_t*>(p.out)[(size_t(seg.b) * hq + g * group + h) * D + d] = f32_to_bf16(ov / l);
+      } else {
+        const size_t ps = (size_t(blockIdx.x) * 2 + slot) * GB + h;
+        p.ws_o[ps * D + d] = ov;
+        if (d == 0) {
+          p.ws_ml[ps * 2] = mm;
+          p.ws_ml[ps * 2 + 1] = l;
+        }
+      }
+    }
+    __syncthreads();  // LDS is reused by the next run
+
+    first_run = false;
+    t = run_end;
+    if (t < t_end) {
+      seg.base = seg_end;
+      if (++seg.sr == spr) {
+        seg.sr = 0;
+        do {
+          ++seg.b;
+          seg.nt = row_tiles(p.kv.seqlens, seg.b, p.kv.max_seq);
+        } while (seg.nt == 0);
+      }
+    }
+  }
+}
+
 // Fold the partials of one (segment, query head): one workgroup each.
 template <int D, int GB>
 __global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p) {
@@ -672,11 +977,25 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_q8(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((decode_q8_mfma_kernel<D>), dim3(p.n_wg), dim3(kWaves * kWave), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long n_comb = (long long)p.kv.batch * p.kv.n_kv_heads * kQ8Cols;
+  hipLaunchKernelGGL((decode_bf16_combine_kernel<D, kQ8Cols>), dim3(unsigned(n_comb)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-int decode_bf16_block(int group) { return group <= 4 ? 4 : 8; }
+int decode_bf16_block(int dtype, int group) {
+  if (dtype == KVC_I8 && group <= kQ8Cols) return kQ8Cols;  // the matrix-core int8 kernel: one block per KV head
+  return group <= 4 ? 4 : 8;
+}
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t s) {
+  if (p.gb == kQ8Cols) return p.kv.head_dim == 128 ? launch_q8<128>(p, s) : launch_q8<64>(p, s);
   if (p.kv.head_dim == 128) return p.gb == 4 ? launch_t<128, 4>(p, s) : launch_t<128, 8>(p, s);
   return p.gb == 4 ? launch_t<64, 4>(p, s) : launch_t<64, 8>(p, s);
 }

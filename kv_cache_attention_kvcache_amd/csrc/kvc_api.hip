@@ -84,7 +84,7 @@ struct DecodePlan {
 DecodePlan decode_plan(const kvc_cache* c, int32_t n_q_heads, int32_t n_workers) {
   DecodePlan pl;
   const int32_t group = n_q_heads / c->n_kv_heads;
-  pl.gb = kvc::decode_bf16_block(group);
+  pl.gb = kvc::decode_bf16_block(c->dtype, group);
   pl.n_hb = (group + pl.gb - 1) / pl.gb;
   pl.n_wg = n_workers > 0 ? n_workers : default_decode_workers();
   return pl;

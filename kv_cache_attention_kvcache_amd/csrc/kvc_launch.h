@@ -64,7 +64,9 @@ struct DecodeParams {
   float scale_log2;
   int32_t* dev_err;
 };
-int decode_bf16_block(int group);                  // query heads per block (4 or 8)
+// Query heads per block: 4 or 8 on vector ALUs; an int8 cache whose group
+// fits 32 heads takes the matrix-core kernel with one 32-head block per KV head.
+int decode_bf16_block(int dtype, int group);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t s);
 
 struct PrefillParams {

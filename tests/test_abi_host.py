@@ -173,10 +173,11 @@ def test_int8_cache_validation(lib):
     assert L.kvc_rope_append(ctypes.byref(bad), 0, q, q, q, q, 1, 16, 1e4, None, None) == lib.KVC_E_ARG
     assert L.kvc_attn_prefill(ctypes.byref(d), 0, q, q, 4, 16, 0.0, None, None) == lib.KVC_E_DTYPE
     assert L.kvc_decode_step(ctypes.byref(d), 0, q, q, q, q, 16, 0.0, 1e4, None, None) == lib.KVC_E_DTYPE
-    # the int8 decode shares the bfloat16 plan and workspace
-    bf = _desc(lib)
+    # the int8 decode on matrix cores keeps one 32-head block per KV head (group <= 32); a larger
+    # group takes the vector kernel's 8-head blocks, like bfloat16
     W = L.kvc_decode_workspace_bytes
-    assert W(ctypes.byref(d), 16, 10) == W(ctypes.byref(bf), 16, 10) > 0
+    assert W(ctypes.byref(d), 16, 10) == 10 * 2 * 32 * 130 * 4
+    assert W(ctypes.byref(d), 4 * 40, 10) == W(ctypes.byref(_desc(lib)), 4 * 40, 10) == 10 * 2 * 8 * 130 * 4
     src = _desc(lib, batch=1, dtype=lib.KVC_I8)
     src.k_scale, src.v_scale = 0x50000, 0x60000
     assert L.kvc_prefill_clone(ctypes.byref(src), 10, ctypes.byref(_desc(lib, batch=8)), None,
