@@ -597,7 +597,11 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
 //     probability that weights its codes in P*V; the softmax sum takes the
 //     unscaled probability.  Lazy running max per head as in the vector path.
 //   * V^T in LDS as bfloat16 key pairs per head dim; O^T += V^T P^T.
-constexpr int kQ8Cols = 32;  // query heads per segment (MFMA columns)
+constexpr int kQ8Cols = kDecodeQ8Block;  // query heads per segment (MFMA columns)
+#ifndef KVC_Q8_STAGES
+#define KVC_Q8_STAGES 2
+#endif
+constexpr int kQ8Stages = KVC_Q8_STAGES;  // tiles in flight per wave
 
 // Tile row fed as A-operand row i so that output register r of lane (column,
 // half h) holds key 16 (r >> 3) + 8 h + (r & 7).
@@ -611,12 +615,15 @@ __device__ __forceinline__ uint32_t i8_pair_bf16(uint32_t w, int byte) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * kWave, 1) void decode_q8_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kWaves * kWave, 2) void decode_q8_mfma_kernel(DecodeParams p) {
+  // Compiled for two workgroups per CU, which caps a wave at 256 registers and keeps every
+  // MFMA operand in VGPRs (a 512-register budget brings AGPR copies); launched one per CU,
+  // which streams faster.
   constexpr int GB = kQ8Cols;
   constexpr int kM = D / 32;                      // 16-byte K loads per lane per tile
   constexpr int kKD = D / 16;                     // MFMA k-steps of S^T
   constexpr int kDB = D / 32;                     // 32-dim blocks of O^T
-  constexpr int kVItems = 16 * (D / 8) / kWave;   // (key pair, 8-dim group) items per lane
+  constexpr int kVItems = 16 * (D / 16) / kWave;  // (key pair, 16-dim group) items per lane
   constexpr int kVStride = 80;                    // bytes per head-dim row of V^T: 16 key pairs + pad
   constexpr int kWaveLds = D * kVStride + 64 * 4;
   constexpr int kMerge = kWaves * GB * (D + 2) * 4;
@@ -690,7 +697,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_q8_mfma_kernel(Decod
     };
     struct Stage {
       u32x4_t k[kM];
-      u32x2_t v[kVItems][2];
+      u32x4_t v[kVItems][2];
       float ks, vs;
     };
     auto issue = [&](int j, Stage& st) {
@@ -704,9 +711,9 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_q8_mfma_kernel(Decod
 #pragma unroll
       for (int it = 0; it < kVItems; ++it) {
         const int i = lane + kWave * it;
-        const int kp = i & 15, dg = i >> 4;
-        st.v[it][0] = __builtin_amdgcn_raw_buffer_load_b64(rv, 2 * kp * row_bytes + 8 * dg, 0, 0);
-        st.v[it][1] = __builtin_amdgcn_raw_buffer_load_b64(rv, (2 * kp + 1) * row_bytes + 8 * dg, 0, 0);
+        const int kp = i & 15, dg = i >> 4;  // lanes of one key pair read consecutive 16-dim groups
+        st.v[it][0] = __builtin_amdgcn_raw_buffer_load_b128(rv, 2 * kp * row_bytes + 16 * dg, 0, 0);
+        st.v[it][1] = __builtin_amdgcn_raw_buffer_load_b128(rv, (2 * kp + 1) * row_bytes + 16 * dg, 0, 0);
       }
       const __amdgpu_buffer_rsrc_t rks = rsrc_at(ksseg, j, 4, hkv * 4);
       const __amdgpu_buffer_rsrc_t rvs = rsrc_at(vsseg, j, 4, hkv * 4);
@@ -721,54 +728,45 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_q8_mfma_kernel(Decod
         const int i = lane + kWave * it;
         const int kp = i & 15, dg = i >> 4;
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const uint32_t wa = dd < 4 ? st.v[it][0].x : st.v[it][0].y;
-          const uint32_t wb = dd < 4 ? st.v[it][1].x : st.v[it][1].y;
+        for (int dd = 0; dd < 16; ++dd) {
+          const uint32_t wa = st.v[it][0][dd >> 2], wb = st.v[it][1][dd >> 2];
           const int sh = 8 * (dd & 3);
-          *reinterpret_cast<uint32_t*>(vt + (8 * dg + dd) * kVStride + 4 * kp) =
+          *reinterpret_cast<uint32_t*>(vt + (16 * dg + dd) * kVStride + 4 * kp) =
               pack_bf16x2(static_cast<float>(static_cast<int8_t>(wa >> sh)),
                           static_cast<float>(static_cast<int8_t>(wb >> sh)));
         }
       }
       scl[lane] = half ? st.vs : st.ks;  // K scale of key l32, or V scale of key l32
-      // ---- K A operands from this stage; then the stage takes tile j_next
-      u32x4_t ka[kKD];
+      // ---- S^T = K Q^T, each K code run widened to its two A operands just before use
+      f32x16_t s;
 #pragma unroll
       for (int m = 0; m < kM; ++m) {
         const u32x4_t w = st.k[m];
-        ka[2 * m] = u32x4_t{i8_pair_bf16(w.x, 0), i8_pair_bf16(w.x, 2), i8_pair_bf16(w.y, 0), i8_pair_bf16(w.y, 2)};
-        ka[2 * m + 1] = u32x4_t{i8_pair_bf16(w.z, 0), i8_pair_bf16(w.z, 2), i8_pair_bf16(w.w, 0), i8_pair_bf16(w.w, 2)};
+        const u32x4_t a0 = {i8_pair_bf16(w.x, 0), i8_pair_bf16(w.x, 2), i8_pair_bf16(w.y, 0), i8_pair_bf16(w.y, 2)};
+        const u32x4_t a1 = {i8_pair_bf16(w.z, 0), i8_pair_bf16(w.z, 2), i8_pair_bf16(w.w, 0), i8_pair_bf16(w.w, 2)};
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0),
+                                                    __builtin_bit_cast(bf16x8_t, qb[2 * m]),
+                                                    m == 0 ? f32x16_t{} : s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1),
+                                                    __builtin_bit_cast(bf16x8_t, qb[2 * m + 1]), s, 0, 0, 0);
       }
-      const float ks_l = st.ks, vs_l = st.vs;
-      (void)ks_l;
-      (void)vs_l;
-      if (j_next >= 0) issue(j_next, st);
-      // ---- S^T = K Q^T
-      f32x16_t s;
-#pragma unroll
-      for (int kd = 0; kd < kKD; ++kd)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[kd]),
-                                                    __builtin_bit_cast(bf16x8_t, qb[kd]),
-                                                    kd == 0 ? f32x16_t{} : s, 0, 0, 0);
+      if (j_next >= 0) issue(j_next, st);  // the stage's codes are consumed: it takes tile j_next
       wave_lds_fence();  // V^T and the scales are visible to the whole wave
-      // ---- softmax of head l32 over this lane's 16 keys: key(r) = 16 (r >> 3) + 8 half + (r & 7)
+      // ---- softmax of head l32 over this lane's 16 keys: key(r) = 16 (r >> 3) + 8 half + (r & 7),
+      // register r of the scores (scaled in place); scales read from LDS four at a time
       const int key0 = j * kTileKeys;
-      float ks[16], vs[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int k4 = 16 * (q4 >> 1) + 8 * half + 4 * (q4 & 1);
-        const float4 a = *reinterpret_cast<const float4*>(scl + k4);
-        const float4 b = *reinterpret_cast<const float4*>(scl + 32 + k4);
-        ks[4 * q4] = a.x; ks[4 * q4 + 1] = a.y; ks[4 * q4 + 2] = a.z; ks[4 * q4 + 3] = a.w;
-        vs[4 * q4] = b.x; vs[4 * q4 + 1] = b.y; vs[4 * q4 + 2] = b.z; vs[4 * q4 + 3] = b.w;
-      }
-      float y[16];
       float tm = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 16 * (r >> 3) + 8 * half + (r & 7);
-        y[r] = key < L ? s[r] * (c * ks[r]) : -INFINITY;
-        tm = fmaxf(tm, y[r]);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 a = *reinterpret_cast<const float4*>(scl + 16 * (q4 >> 1) + 8 * half + 4 * (q4 & 1));
+        const float kk[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * q4 + u;
+          const int key = key0 + 16 * (r >> 3) + 8 * half + (r & 7);
+          s[r] = key < L ? s[r] * (c * kk[u]) : -INFINITY;
+          tm = fmaxf(tm, s[r]);
+        }
       }
       tm = fmaxf(tm, __shfl_xor(tm, 32));  // the head's max over the tile (both halves)
       if (__ballot(tm > mh + kLazyLog2)) {
@@ -784,13 +782,16 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_q8_mfma_kernel(Decod
       u32x4_t pf[2];
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const float4 b0 = *reinterpret_cast<const float4*>(scl + 32 + 16 * ks2 + 8 * half);
+        const float4 b1 = *reinterpret_cast<const float4*>(scl + 32 + 16 * ks2 + 8 * half + 4);
+        const float vv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 8 * ks2 + 2 * i;
-          const float p0 = exp2f(y[r] - mh), p1 = exp2f(y[r + 1] - mh);
+          const float p0 = exp2f(s[r] - mh), p1 = exp2f(s[r + 1] - mh);
           lpart += p0 + p1;
-          w[i] = pack_bf16x2(p0 * vs[r], p1 * vs[r + 1]);
+          w[i] = pack_bf16x2(p0 * vv[2 * i], p1 * vv[2 * i + 1]);
         }
         pf[ks2] = u32x4_t{w[0], w[1], w[2], w[3]};
       }
@@ -805,18 +806,20 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_q8_mfma_kernel(Decod
         }
     };
 
-    // The wave's tiles of this run: j0 + wave, j0 + wave + 4, ...; two stages in flight.
-    Stage sa, sb;
+    // The wave's tiles of this run: j0 + wave, j0 + wave + 4, ...; kQ8Stages tiles in flight
+    // (one wave per SIMD: the bytes in flight, not the ALUs, set the streaming rate).
+    Stage st[kQ8Stages];
     int j = j0 + wave;
-    if (j < j1) issue(j, sa);
-    if (j + kWaves < j1) issue(j + kWaves, sb);
+#pragma unroll
+    for (int i = 0; i < kQ8Stages; ++i)
+      if (j + i * kWaves < j1) issue(j + i * kWaves, st[i]);
     auto next = [&](int jj) { return jj < j1 ? jj : -1; };
     while (j < j1) {
-      process(j, sa, next(j + 2 * kWaves));
-      j += kWaves;
-      if (j >= j1) break;
-      process(j, sb, next(j + 2 * kWaves));
-      j += kWaves;
+#pragma unroll
+      for (int i = 0; i < kQ8Stages; ++i) {
+        if (j < j1) process(j, st[i], next(j + kQ8Stages * kWaves));
+        j += kWaves;
+      }
     }
 
     // ---- fold the four waves' states of this run (as decode_bf16_kernel, 32 heads)

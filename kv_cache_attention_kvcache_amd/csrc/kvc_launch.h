@@ -67,6 +67,7 @@ struct DecodeParams {
 // Query heads per block: 4 or 8 on vector ALUs; an int8 cache whose group
 // fits 32 heads takes the matrix-core kernel with one 32-head block per KV head.
 int decode_bf16_block(int dtype, int group);
+constexpr int kDecodeQ8Block = 32;  // the matrix-core int8 kernel's query-head block
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t s);
 
 struct PrefillParams {
