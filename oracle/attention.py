@@ -164,3 +164,25 @@ def cache_bytes(n_layers: int, tokens: int, n_kv_heads: int, head_dim: int, byte
 def prefill_units(prompt_len: int, n_samples: int, clone: bool) -> int:
     """The nanochat post's prefill cost units: N x prompt^2 naive, 1 x prompt^2 with the clone."""
     return (1 if clone else n_samples) * prompt_len * prompt_len
+
+
+def window_outputs(q_raw, k_raw, v_raw, query_positions, window: int, dtype: str,
+                   base: float = 10000.0, scale: float | None = None) -> np.ndarray:
+    """No-cache attention of selected positions over a sliding window of positions.
+
+    Tiny-GPT post, "The Cache, in Code" and "Does the Cache Change the Output?":
+    the rolling cache keeps the last `window` positions, each rotated at its
+    absolute position, and the query at position p attends keys
+    max(0, p + 1 - window) .. p.  Every key is re-rotated here from its raw
+    value at its absolute position.  Returns (len(query_positions), Hq, D).
+    """
+    query_positions = np.asarray(query_positions, dtype=np.int64)
+    outs = []
+    for p in query_positions:
+        lo = max(0, int(p) + 1 - window)
+        pos = np.arange(lo, int(p) + 1)
+        k_hat = rotate_round(round_to(np.asarray(k_raw, dtype=np.float64)[lo:p + 1], dtype), pos, dtype, base)
+        v = round_to(np.asarray(v_raw, dtype=np.float64)[lo:p + 1], dtype)
+        q_hat = rotate_round(round_to(np.asarray(q_raw, dtype=np.float64)[p][None], dtype), [int(p)], dtype, base)
+        outs.append(attend(q_hat, k_hat, v, [len(pos) - 1], scale)[0])
+    return np.stack(outs)
