@@ -23,6 +23,19 @@
  * KVC_F32 or KVC_BF16 (bfloat16, round to nearest even).  All accumulation
  * is in float32.  head_dim must be 64 or 128.
  *
+ * Rolling window (rolling = 1).  Tiny-GPT post, "The Cache, in Code" and "Does
+ * the Cache Change the Output?": the cache keeps the last max_seq positions,
+ * each rotated at its absolute position; attention scores depend only on the
+ * distance between query and key, so the window can slide without
+ * re-rotating.  seqlens[b] then counts every token row b has seen, and
+ * absolute position p lives in slot p mod max_seq.  kvc_rope_append writes
+ * token t at slot (P + t) mod max_seq (T <= max_seq, else KVC_E_ARG), rotated
+ * at P + t; a one-token decode (kvc_attn_decode, kvc_decode_step) attends the
+ * min(P + 1, max_seq) filled slots -- positions max(0, P + 1 - max_seq) .. P,
+ * order being irrelevant to softmax.  kvc_attn_prefill keeps the linear rule
+ * P + T <= max_seq for every T, so a prompt is prefilled before the window
+ * first wraps; the clone copies slots [0, src_len) as in a linear cache.
+ *
  * 8-bit cache (KVC_I8).  Cake paper, Section 5.1 ("Compression methods") and
  * Section 5.5 (Table 6): the KV cache can be kept in 8 bits, which halves the
  * bytes decode must stream.  K and V then hold int8 codes, and k_scale /
@@ -90,6 +103,7 @@ typedef struct kvc_cache {
   int32_t dtype;    /* KVC_F32, KVC_BF16 or KVC_I8 */
   float* k_scale;   /* KVC_I8 only: device, (n_layers, batch, max_seq, n_kv_heads); else ignored */
   float* v_scale;   /* KVC_I8 only: device, same shape */
+  int32_t rolling;  /* 0: linear cache; 1: rolling window of max_seq positions (see below) */
 } kvc_cache;
 
 /*

@@ -42,7 +42,7 @@ class kvc_cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("seqlens", ctypes.c_void_p),
                 ("n_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("rolling", ctypes.c_int32)]
 
 
 def _load():
@@ -102,10 +102,13 @@ class KVCache:
     bfloat16 or int8 (codes), contiguous, on one GPU; seqlens: (batch,) int32
     on that GPU.  An int8 cache also takes k_scale, v_scale: float32
     (n_layers, batch, max_seq, n_kv_heads), one scale per cached vector; its
-    queries and outputs are bfloat16.
+    queries and outputs are bfloat16.  rolling=True keeps a window of the last
+    max_seq positions: position p in slot p mod max_seq, seqlens counting every
+    token seen.
     """
 
-    def __init__(self, k: torch.Tensor, v: torch.Tensor, seqlens: torch.Tensor, k_scale=None, v_scale=None):
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, seqlens: torch.Tensor, k_scale=None, v_scale=None,
+                 rolling: bool = False):
         if k.shape != v.shape or k.dim() != 5 or k.dtype != v.dtype or k.dtype not in _DTYPE_CODE:
             raise ValueError("k and v must be matching 5-d float32/bfloat16/int8 tensors")
         if not (k.is_contiguous() and v.is_contiguous()) or not (k.is_cuda and v.is_cuda):
@@ -123,15 +126,17 @@ class KVCache:
         self._desc = kvc_cache(k.data_ptr(), v.data_ptr(), seqlens.data_ptr(), *[int(s) for s in k.shape],
                                _DTYPE_CODE[k.dtype],
                                self.k_scale.data_ptr() if self.k_scale is not None else None,
-                               self.v_scale.data_ptr() if self.v_scale is not None else None)
+                               self.v_scale.data_ptr() if self.v_scale is not None else None, int(bool(rolling)))
+        self.rolling = bool(rolling)
 
     @classmethod
-    def empty(cls, n_layers, batch, max_seq, n_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda"):
+    def empty(cls, n_layers, batch, max_seq, n_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda",
+              rolling: bool = False):
         shape = (n_layers, batch, max_seq, n_kv_heads, head_dim)
         scales = (torch.zeros(shape[:4], dtype=torch.float32, device=device),
                   torch.zeros(shape[:4], dtype=torch.float32, device=device)) if dtype == torch.int8 else (None, None)
         return cls(torch.empty(shape, dtype=dtype, device=device), torch.empty(shape, dtype=dtype, device=device),
-                   torch.zeros(batch, dtype=torch.int32, device=device), *scales)
+                   torch.zeros(batch, dtype=torch.int32, device=device), *scales, rolling=rolling)
 
     @property
     def n_layers(self):

@@ -75,12 +75,11 @@ __global__ __launch_bounds__(256, 1) void split_attention_kernel(SplitParams p) 
   const int b = row / p.T;
   const int t = row - b * p.T;
 
-  const int start = p.kv.seqlens[b];
-  if (start < 0 || start > p.kv.max_seq - p.T) {
+  const int n_keys = attended_keys(p.kv, p.kv.seqlens[b], p.T, t);  // keys 0 .. start + t
+  if (n_keys < 0) {
     if (split == 0 && hb_all == 0 && t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
     return;
   }
-  const int n_keys = start + t + 1;  // keys 0 .. start + t
   const int k_begin = split * p.split_keys;
   if (k_begin >= n_keys) return;
   const int k_end = min(k_begin + p.split_keys, n_keys);
@@ -323,9 +322,8 @@ __global__ __launch_bounds__(64) void split_combine_kernel(SplitParams p) {
   const int row = qh / p.n_q_heads;
   const int b = row / p.T;
   const int t = row - b * p.T;
-  const int start = p.kv.seqlens[b];
-  if (start < 0 || start > p.kv.max_seq - p.T) return;
-  const int n_keys = start + t + 1;
+  const int n_keys = attended_keys(p.kv, p.kv.seqlens[b], p.T, t);
+  if (n_keys < 0) return;
   const int n_split = (n_keys + p.split_keys - 1) / p.split_keys;
   if (n_split <= 1) return;  // written directly by the split pass
   const float* ml = p.ws_ml + size_t(qh) * p.max_splits * 2;

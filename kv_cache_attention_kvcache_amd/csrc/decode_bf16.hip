@@ -7,7 +7,8 @@
 // at a GQA group of 8 -- so nothing is reshaped into matrix-core work.
 //
 // Work partition.  A segment is (row b, KV head g, block hb of GB query heads
-// of its group); it holds ceil(L_b / 32) tiles of 32 keys, L_b = seqlens[b]+1.
+// of its group); it holds ceil(L_b / 32) tiles of 32 keys, L_b = seqlens[b]+1
+// (min(seqlens[b]+1, max_seq) filled slots in a rolling window).
 // All segments laid end to end form N tiles; the grid is persistent (one
 // workgroup per CU by default) and workgroup w takes the tiles
 // [w N / P, (w+1) N / P) -- the same K/V bytes per workgroup whatever the
@@ -164,11 +165,11 @@ struct Elem<true> {  // int8 codes: 8 bytes, widened exactly (|code| <= 127 fits
   }
 };
 
-// Number of 32-key tiles of row b, or 0 if its length is out of range.
-__device__ __forceinline__ int row_tiles(const int32_t* seqlens, int b, int max_seq) {
-  const int p = seqlens[b];
-  if (p < 0 || p > max_seq - 1) return 0;
-  return (p + kTileKeys) / kTileKeys;  // ceil((p + 1) / 32)
+// Keys row b's decode query attends (-1: out of range), and their 32-key tiles (0 if out of range).
+__device__ __forceinline__ int row_keys(const LayerView& kv, int b) { return attended_keys(kv, kv.seqlens[b], 1, 0); }
+__device__ __forceinline__ int row_tiles(const LayerView& kv, int b) {
+  const int n = row_keys(kv, b);
+  return n < 0 ? 0 : (n + kTileKeys - 1) / kTileKeys;
 }
 
 // The value of lane 0, known to the compiler to be wave-uniform (an SGPR).
@@ -198,7 +199,7 @@ __device__ int total_tiles(const DecodeParams& p, int lane) {
   int n = 0;
   for (int b0 = 0; b0 < p.kv.batch; b0 += kWave) {
     const int b = b0 + lane;
-    n += wave_sum_i(b < p.kv.batch ? row_tiles(p.kv.seqlens, b, p.kv.max_seq) : 0);
+    n += wave_sum_i(b < p.kv.batch ? row_tiles(p.kv, b) : 0);
   }
   return n * p.kv.n_kv_heads * p.n_hb;
 }
@@ -208,7 +209,7 @@ __device__ SegPos find_segment(const DecodeParams& p, int t, int lane) {
   int cum = 0;
   for (int b0 = 0; b0 < p.kv.batch; b0 += kWave) {
     const int b = b0 + lane;
-    const int nt = b < p.kv.batch ? row_tiles(p.kv.seqlens, b, p.kv.max_seq) : 0;
+    const int nt = b < p.kv.batch ? row_tiles(p.kv, b) : 0;
     const int incl = wave_incl_scan_i(nt * spr, lane);
     const int total = uniform(__shfl(incl, kWave - 1));
     if (cum + total > t) {
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
     const bool complete = t == seg.base && run_end == seg_end;
     const int g = seg.sr / p.n_hb;
     const int hb = seg.sr - g * p.n_hb;
-    const int L = p.kv.seqlens[seg.b] + 1;
+    const int L = row_keys(p.kv, seg.b);  // >= 1: the run has tiles
     const int j0 = t - seg.base, j1 = run_end - seg.base;  // local tiles of the run
 
     // Segment bases (row b, position 0, KV head g).
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
         seg.sr = 0;
         do {
           ++seg.b;
-          seg.nt = row_tiles(p.kv.seqlens, seg.b, p.kv.max_seq);
+          seg.nt = row_tiles(p.kv, seg.b);
         } while (seg.nt == 0);
       }
     }
@@ -659,7 +660,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_q8_mfma_kernel(Decod
     const int run_end = min(t_end, seg_end);
     const bool complete = t == seg.base && run_end == seg_end;
     const int g = seg.sr;
-    const int L = p.kv.seqlens[seg.b] + 1;
+    const int L = row_keys(p.kv, seg.b);  // >= 1: the run has tiles
     const int j0 = t - seg.base, j1 = run_end - seg.base;
 
     const size_t vec0 = size_t(seg.b) * p.kv.max_seq * hkv + g;
@@ -873,7 +874,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_q8_mfma_kernel(Decod
         seg.sr = 0;
         do {
           ++seg.b;
-          seg.nt = row_tiles(p.kv.seqlens, seg.b, p.kv.max_seq);
+          seg.nt = row_tiles(p.kv, seg.b);
         } while (seg.nt == 0);
       }
     }
@@ -901,7 +902,7 @@ __global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
 
-  const int nt = row_tiles(p.kv.seqlens, b, p.kv.max_seq);
+  const int nt = row_tiles(p.kv, b);
   if (nt == 0) {
     if (sr == 0 && h == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
     return;
@@ -911,7 +912,7 @@ __global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p
   int n_all = 0, before = 0;
   for (int b0 = 0; b0 < p.kv.batch; b0 += kWave) {
     const int bb = b0 + lane;
-    const int v = bb < p.kv.batch ? row_tiles(p.kv.seqlens, bb, p.kv.max_seq) : 0;
+    const int v = bb < p.kv.batch ? row_tiles(p.kv, bb) : 0;
     n_all += wave_sum_i(v);
     before += wave_sum_i(bb < b ? v : 0);
   }

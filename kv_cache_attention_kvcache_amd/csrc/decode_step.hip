@@ -72,8 +72,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeStepParams 
   const int b = blockIdx.x / hkv;
   const int g = blockIdx.x - b * hkv;
 
-  const int pos = p.kv.seqlens[b];
-  if (pos < 0 || pos >= p.kv.max_seq) {
+  const int pos = p.kv.seqlens[b];  // absolute position of the new token: its rotation angle
+  const int n_keys = attended_keys(p.kv, pos, 1, 0);
+  if (n_keys < 0) {
     if (g == 0 && tid == 0) report(p.dev_err, KVC_DEV_CAPACITY);
     return;
   }
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeStepParams 
     sn[tid] = s;
   }
   __syncthreads();
-  const size_t slot = ((size_t(b) * p.kv.max_seq + pos) * hkv + g) * D;
+  const size_t slot = ((size_t(b) * p.kv.max_seq + slot_of(p.kv, pos)) * hkv + g) * D;
   for (int e = tid; e < (G + 1) * HALF; e += kThreads) {
     const int hh = e / HALF;  // hh < G: query head g G + hh; hh == G: the key
     const int i = e - hh * HALF;
@@ -112,8 +113,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeStepParams 
   }
   __syncthreads();  // queries in LDS; this workgroup's K/V slot written and visible to it
 
-  // ---- 2. attention over keys 0..pos, online softmax across 256-key tiles.
-  const int n_keys = pos + 1;
+  // ---- 2. attention over the row's filled slots, online softmax across 256-key tiles.
   const size_t key_stride = size_t(hkv) * D;
   const T* k_base = static_cast<const T*>(p.kv.k) + size_t(b) * p.kv.max_seq * key_stride + size_t(g) * D;
   const T* v_base = static_cast<const T*>(p.kv.v) + size_t(b) * p.kv.max_seq * key_stride + size_t(g) * D;

@@ -23,6 +23,7 @@ int check_cache(const kvc_cache* c) {
     return KVC_E_ARG;
   if (c->n_layers < 1 || c->batch < 1 || c->max_seq < 1 || c->n_kv_heads < 1) return KVC_E_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return KVC_E_SHAPE;
+  if (c->rolling != 0 && c->rolling != 1) return KVC_E_ARG;
   return KVC_OK;
 }
 
@@ -46,6 +47,7 @@ kvc::LayerView layer_view(const kvc_cache* c, int32_t layer) {
   v.n_kv_heads = c->n_kv_heads;
   v.head_dim = c->head_dim;
   v.dtype = c->dtype;
+  v.rolling = c->rolling;
   v.k_scale = c->dtype == KVC_I8 ? c->k_scale + size_t(layer) * layer_vecs : nullptr;
   v.v_scale = c->dtype == KVC_I8 ? c->v_scale + size_t(layer) * layer_vecs : nullptr;
   return v;
@@ -118,6 +120,7 @@ int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* 
   if (!(rope_base > 1.f) || isinf(rope_base)) return KVC_E_ARG;
   if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
   if (int64_t(cache->batch) * T > 0x7fffffffLL) return KVC_E_ARG;
+  if (cache->rolling && T > cache->max_seq) return KVC_E_ARG;  // one call must not overwrite its own tokens
   kvc::RopeAppendParams p;
   p.kv = layer_view(cache, layer);
   p.q = q;
@@ -207,11 +210,13 @@ int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, v
   if (!resolve_scale(scale, cache->head_dim, &sc)) return KVC_E_ARG;
   if (cache->dtype == KVC_I8) return KVC_E_DTYPE;  // prefill reads bfloat16 or float32 caches
   hipStream_t s = static_cast<hipStream_t>(stream);
+  kvc::LayerView lv = layer_view(cache, layer);
+  lv.rolling = 0;  // prefill keeps the linear rule P + T <= max_seq, rolling window or not
   if (cache->dtype == KVC_BF16) {
     // The kernel's buffer descriptors span one head row with 32-bit byte offsets.
     if (int64_t(cache->max_seq) * cache->n_kv_heads * cache->head_dim * 2 >= (int64_t(1) << 31)) return KVC_E_SHAPE;
     kvc::PrefillParams p;
-    p.kv = layer_view(cache, layer);
+    p.kv = lv;
     p.q = q_rot;
     p.out = out;
     p.T = T;
@@ -222,7 +227,7 @@ int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, v
   }
   // float32: one split spanning the whole cache per query row, written directly.
   kvc::SplitParams p;
-  p.kv = layer_view(cache, layer);
+  p.kv = lv;
   p.q = q_rot;
   p.out = out;
   p.T = T;

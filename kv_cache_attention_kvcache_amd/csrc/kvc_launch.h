@@ -17,7 +17,24 @@ struct LayerView {
   int32_t batch, max_seq, n_kv_heads, head_dim, dtype;
   float* k_scale;  // int8 caches: (batch, max_seq, n_kv_heads) scales of this layer; else null
   float* v_scale;
+  int32_t rolling;  // rolling window: position p in slot p mod max_seq
 };
+
+// Keys query t (of T new tokens of row b, P = seqlens[b]) attends, or -1 if the
+// row is out of range (skipped, KVC_DEV_CAPACITY).  Linear cache, or T > 1:
+// P + t + 1 while P + T <= max_seq.  Rolling window, T = 1: the min(P + 1, max_seq)
+// filled slots.
+__device__ __forceinline__ int attended_keys(const LayerView& kv, int start, int T, int t) {
+  if (start < 0) return -1;
+  if (kv.rolling && T == 1) return start < kv.max_seq ? start + 1 : kv.max_seq;
+  if (start > kv.max_seq - T) return -1;
+  return start + t + 1;
+}
+
+// Slot of absolute position pos (written by the append of a call with T tokens).
+__device__ __forceinline__ int slot_of(const LayerView& kv, int pos) {
+  return kv.rolling ? pos % kv.max_seq : pos;
+}
 
 struct RopeAppendParams {
   LayerView kv;

@@ -52,11 +52,11 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendParams p) {
   const int b = row / p.T;
   const int t = row - b * p.T;
   const int start = p.kv.seqlens[b];
-  if (start < 0 || start > p.kv.max_seq - p.T) {
+  if (start < 0 || (!p.kv.rolling && start > p.kv.max_seq - p.T)) {
     if (t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
     return;
   }
-  const int pos = start + t;
+  const int pos = start + t;  // absolute position: the rotation angle
   if (threadIdx.x < HALF) {
     // One float32 product, as the angle table is built; full-range sincos.
     const float theta = __fmul_rn(static_cast<float>(pos), p.inv_freq[threadIdx.x]);
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendParams p) {
   const T* q_row = static_cast<const T*>(p.q) + size_t(row) * hq * D;
   T* q_out_row = static_cast<T*>(p.q_out) + size_t(row) * hq * D;
   const T* k_row = static_cast<const T*>(p.k_new) + size_t(row) * hkv * D;
-  const size_t slot = (size_t(b) * p.kv.max_seq + pos) * hkv * D;
+  const size_t slot = (size_t(b) * p.kv.max_seq + slot_of(p.kv, pos)) * hkv * D;
   T* k_slot = static_cast<T*>(p.kv.k) + slot;
 
   const int n_items = (hq + hkv) * QUADS;
@@ -120,11 +120,11 @@ __global__ __launch_bounds__(256) void rope_append_q8_kernel(RopeAppendParams p)
   const int b = row / p.T;
   const int t = row - b * p.T;
   const int start = p.kv.seqlens[b];
-  if (start < 0 || start > p.kv.max_seq - p.T) {
+  if (start < 0 || (!p.kv.rolling && start > p.kv.max_seq - p.T)) {
     if (t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
     return;
   }
-  const int pos = start + t;
+  const int pos = start + t;  // absolute position: the rotation angle
   if (threadIdx.x < HALF) {
     const float theta = __fmul_rn(static_cast<float>(pos), p.inv_freq[threadIdx.x]);
     float s, c;
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void rope_append_q8_kernel(RopeAppendParams p)
 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const size_t vec0 = (size_t(b) * p.kv.max_seq + pos) * hkv;  // this position's first (head) vector
+  const size_t vec0 = (size_t(b) * p.kv.max_seq + slot_of(p.kv, pos)) * hkv;  // this slot's first (head) vector
   for (int vi = wave; vi < 2 * hkv; vi += blockDim.x / kWave) {
     const bool is_k = vi < hkv;
     const int g = is_k ? vi : vi - hkv;

@@ -67,21 +67,22 @@ def appended_slots_int8(k_raw, v_raw, start: int, base: float = 10000.0):
 
 
 def decode_over_int8(k_codes, k_scales, v_codes, v_scales, q_raw, k_raw, v_raw, base: float = 10000.0,
-                     scale: float | None = None) -> np.ndarray:
-    """One decode token over a row whose first P positions hold int8 codes and scales.
+                     scale: float | None = None, position: int | None = None) -> np.ndarray:
+    """One decode token over a row's stored int8 history.
 
-    k_codes/v_codes (P, Hkv, D), k_scales/v_scales (P, Hkv): the stored
+    k_codes/v_codes (n, Hkv, D), k_scales/v_scales (n, Hkv): the stored
     (already rotated) history.  q_raw (Hq, D), k_raw/v_raw (Hkv, D): the new
-    token at position P, whose key and value are quantized as the append
-    stores them.  The query is rotated and rounded to bfloat16 only.
-    Attention in float64 over the dequantized keys and values.  Returns (Hq, D).
+    token at absolute position `position` (default n: a linear cache holding
+    positions 0..n-1), whose key and value are quantized as the append stores
+    them.  The query is rotated and rounded to bfloat16 only.  Attention in
+    float64 over the dequantized keys and values.  Returns (Hq, D).
     """
     from .attention import attend
     from .numerics import round_to
     from .rope import rotate_round
-    p = np.asarray(k_codes).shape[0]
+    p = np.asarray(k_codes).shape[0] if position is None else int(position)
     kc, ks, vc, vs = appended_slots_int8(np.asarray(k_raw)[None], np.asarray(v_raw)[None], p, base)
     k_all = np.concatenate([dequantize_int8(k_codes, k_scales), dequantize_int8(kc, ks)], axis=0)
     v_all = np.concatenate([dequantize_int8(v_codes, v_scales), dequantize_int8(vc, vs)], axis=0)
     q_hat = rotate_round(round_to(np.asarray(q_raw)[None], "bf16"), [p], "bf16", base)
-    return attend(q_hat, k_all, v_all, [p], scale)[0]
+    return attend(q_hat, k_all, v_all, [k_all.shape[0] - 1], scale)[0]

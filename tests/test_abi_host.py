@@ -182,3 +182,14 @@ def test_int8_cache_validation(lib):
     src.k_scale, src.v_scale = 0x50000, 0x60000
     assert L.kvc_prefill_clone(ctypes.byref(src), 10, ctypes.byref(_desc(lib, batch=8)), None,
                                None) == lib.KVC_E_DTYPE  # int8 source, bfloat16 destination
+
+
+def test_rolling_window_validation(lib):
+    L = lib.lib
+    q = P(0x40000)
+    d = _desc(lib)  # max_seq 100
+    d.rolling = 1
+    assert L.kvc_rope_append(ctypes.byref(d), 0, q, q, q, q, 101, 16, 1e4, None, None) == lib.KVC_E_ARG  # T > window
+    bad = _desc(lib)
+    bad.rolling = 2
+    assert L.kvc_attn_decode(ctypes.byref(bad), 0, q, q, 16, 0.0, 0, P(0x70000), 1 << 30, None, None) == lib.KVC_E_ARG
