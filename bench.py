@@ -15,7 +15,13 @@ attention TFLOP/s, tokens/s, a roofline record for the decode kernel pair
 (HIP events around every decode call, on the stream they run on) and the CPU
 oracle timed on a bounded sample of the same work.
 
-    python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline] [--no-ceilings]
+
+After the timed steps the default run also measures two ceilings of the chip
+(kv_cache_attention_kvcache_amd.ceilings): the best streaming-read rate in
+decode's access shape (256-byte rows at a 2 KiB stride) and the best bfloat16
+matrix-core rate, and states each roofline against them as well as against
+the published peaks.
 
 `--workload long_context_int8` runs the same decode steps on an int8 cache
 (codes plus one float32 scale per cached vector): the 72K context is written
@@ -85,6 +91,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps per batch size (default 512)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured-ceiling probes (a streaming read and a matrix-core loop) after the run")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many MiB (a known-size "
@@ -261,6 +269,15 @@ def main():
                              "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
                              "flops_per_step": int(pre_flops), "avg_launch_us": round(ms_pre / (K * n_chunks) * 1e3, 1)},
     }
+    if not args.no_ceilings:
+        from kv_cache_attention_kvcache_amd import ceilings
+        torch.cuda.synchronize()
+        c = ceilings.measure(dev)
+        res["measured_ceilings"] = c
+        for key, probe in (("roofline", "hbm_read_rows_gbps"), ("roofline_prefill", "mfma_bf16_tflops")):
+            res[key]["measured_ceiling"] = c[probe]["value"]
+            res[key]["frac_of_measured"] = round(res[key]["achieved"] / c[probe]["value"], 4)
+        log(f"measured ceilings: {c}", q_)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -2,7 +2,9 @@
 
 Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
 parallel), then they are linked into ``libkvc.so`` next to this file.  The
-library is replaced atomically so a running process never loads a half
+measured-ceiling kernels (``ceilings/*.hip``) go into their own
+``ceilings/libkvc_ceilings.so``, so libkvc exports only the attention calls.
+Each library is replaced atomically so a running process never loads a half
 written file.
 """
 from __future__ import annotations
@@ -19,6 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libkvc.so")
+CEIL_DIR = os.path.join(HERE, "ceilings")
+CEIL_LIB_PATH = os.path.join(CEIL_DIR, "libkvc_ceilings.so")
 
 ARCH = "gfx950"
 FLAGS = [
@@ -37,30 +41,36 @@ def hipcc() -> str:
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    obj = os.path.join(BUILD_DIR, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src) + ".o")
+    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", os.path.dirname(src), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every kernel source and link libkvc.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    if not srcs:
-        raise RuntimeError("no HIP sources found")
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+def _link(objs, path: str) -> None:
+    tmp = path + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every kernel source, link libkvc.so and libkvc_ceilings.so; returns libkvc's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    ceil_srcs = sorted(glob.glob(os.path.join(CEIL_DIR, "*.hip")))
+    if not srcs or not ceil_srcs:
+        raise RuntimeError("no HIP sources found")
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(ceil_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs + ceil_srcs))
+    _link(objs[:len(srcs)], LIB_PATH)
+    _link(objs[len(srcs):], CEIL_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources")
+        print(f"built {LIB_PATH} from {len(srcs)} sources and {CEIL_LIB_PATH}")
     return LIB_PATH
 
 

@@ -1,0 +1,118 @@
+"""Measured ceilings of the GPU: a streaming read and a matrix-core loop.
+
+A ctypes binding over ``libkvc_ceilings.so`` (declared in ``ceilings.h``) and
+``measure()``, which times the two probes with HIP events on torch's current
+stream.  The attention kernels' rates can then be stated against what this
+chip measurably reaches, next to the published peaks.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc_ceilings.so")
+EXPORTS = ("kvc_ceiling_stream_read", "kvc_ceiling_mfma_bf16")
+MFMA_FLOPS = 32768  # one 32x32x16 product: 2 * 32 * 32 * 16 flops
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.kvc_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        lib.kvc_ceiling_stream_read.restype = ctypes.c_int
+        lib.kvc_ceiling_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+        lib.kvc_ceiling_mfma_bf16.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _stream_ptr():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def stream_read(buf: torch.Tensor, row_bytes: int, stride_bytes: int, nontemporal: bool, workgroups: int,
+                sink: torch.Tensor) -> int:
+    """Launch one streaming read over buf (a contiguous uint8 device tensor); returns the bytes read."""
+    if buf.dtype != torch.uint8 or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous uint8 device tensor")
+    rows = buf.numel() // stride_bytes
+    rc = _load().kvc_ceiling_stream_read(ctypes.c_void_p(buf.data_ptr()), rows, row_bytes, stride_bytes,
+                                         int(nontemporal), workgroups, ctypes.c_void_p(sink.data_ptr()),
+                                         _stream_ptr())
+    if rc != 0:
+        raise RuntimeError(f"kvc_ceiling_stream_read failed ({rc})")
+    return rows * row_bytes
+
+
+def mfma_bf16(iters: int, chains: int, workgroups: int, sink: torch.Tensor) -> float:
+    """Launch the matrix-core loop; returns its flops."""
+    rc = _load().kvc_ceiling_mfma_bf16(iters, chains, workgroups, ctypes.c_void_p(sink.data_ptr()),
+                                       _stream_ptr())
+    if rc != 0:
+        raise RuntimeError(f"kvc_ceiling_mfma_bf16 failed ({rc})")
+    return float(workgroups) * 4 * iters * chains * MFMA_FLOPS
+
+
+def _timed(fn, reps: int) -> float:
+    """Seconds per call: one untimed call, then `reps` calls between HIP events on the current stream."""
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def measure(device=None, buffer_gib: int = 4, reps: int = 5) -> dict:
+    """The best rate of each probe over its launch shapes.
+
+    * hbm_read_gbps: contiguous 16-byte loads over `buffer_gib` GiB (far past
+      the 256 MB last-level cache), with and without the non-temporal hint.
+    * hbm_read_rows_gbps: decode's access shape, 256-byte rows at a 2 KiB
+      stride (one KV head's row of a bfloat16 cache with 8 KV heads of 128
+      dims), the bytes of the rows only.
+    * mfma_bf16_tflops: two or four independent 32x32x16 bfloat16 chains
+      per wave, one or two 4-wave workgroups per CU (one or two waves per
+      SIMD).
+    """
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    with torch.cuda.device(dev):
+        buf = torch.empty(buffer_gib << 30, dtype=torch.uint8, device=dev)
+        buf.fill_(1)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        shapes = {}
+        for name, row, stride in (("hbm_read_gbps", 256, 256), ("hbm_read_rows_gbps", 256, 2048)):
+            best = 0.0
+            for nt in (False, True):
+                for wpc in (1, 2, 4):
+                    nbytes = (buf.numel() // stride) * row
+                    t = _timed(lambda: stream_read(buf, row, stride, nt, cus * wpc, sink), reps)
+                    rate = nbytes / t / 1e9
+                    if rate > best:
+                        best, shapes[name] = rate, {"nontemporal": nt, "workgroups_per_cu": wpc}
+            shapes[name]["value"] = round(best, 1)
+        del buf
+        best = 0.0
+        for chains in (2, 4):
+            for wpc in (1, 2):
+                iters = 80000 // chains
+                fl = float(cus * wpc) * 4 * iters * chains * MFMA_FLOPS
+                t = _timed(lambda: mfma_bf16(iters, chains, cus * wpc, sink), reps)
+                rate = fl / t / 1e12
+                if rate > best:
+                    best, shapes["mfma_bf16_tflops"] = rate, {"chains": chains, "workgroups_per_cu": wpc}
+        shapes["mfma_bf16_tflops"]["value"] = round(best, 1)
+    return shapes

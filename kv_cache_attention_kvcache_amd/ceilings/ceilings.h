@@ -1,0 +1,39 @@
+// Measured ceilings of one MI355X: what a plain streaming read and a plain
+// matrix-core loop reach on this chip, so that the attention kernels'
+// bandwidth and TFLOP/s can be stated against measured limits as well as the
+// published ones (8 TB/s HBM3E, 2.5 PFLOP/s dense bfloat16).
+//
+// This library is measurement infrastructure, separate from libkvc: it holds
+// no part of the attention method.  Both calls are asynchronous on `stream`,
+// allocate nothing and return 0 or a negative code (-1: bad argument, before
+// any launch; -2: launch failure).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+// Reads `rows` rows of `row_bytes` bytes, row r starting at buf + r * stride_bytes,
+// with 16-byte vector loads, 16 lanes per 256 bytes, and folds every word into an
+// XOR that is written to *sink only if it equals a value no test data produces
+// (so the loads cannot be removed).  row_bytes is a positive multiple of 256 and
+// at most stride_bytes; buf is 16-byte aligned and holds rows * stride_bytes bytes
+// (device memory, owned by the caller).  `nontemporal` != 0 puts the
+// non-temporal hint on every load.  `workgroups` persistent workgroups of 256
+// threads share the rows evenly.
+int kvc_ceiling_stream_read(const void* buf, int64_t rows, int32_t row_bytes, int64_t stride_bytes,
+                            int32_t nontemporal, int32_t workgroups, uint32_t* sink, hipStream_t stream);
+
+// Every wave of `workgroups` workgroups of 256 threads runs `iters` rounds of
+// `chains` (2 or 4) independent v_mfma_f32_32x32x16_bf16 accumulations
+// (32768 flops each); *sink is written only for an impossible result.
+// Flops per call = workgroups * 4 waves * iters * chains * 32768.
+int kvc_ceiling_mfma_bf16(int32_t iters, int32_t chains, int32_t workgroups, float* sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif

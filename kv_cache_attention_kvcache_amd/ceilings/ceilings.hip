@@ -1,0 +1,93 @@
+// Streaming-read and matrix-core ceiling kernels (declared in ceilings.h).
+#include "ceilings.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kLoadsInFlight = 8;  // 16-byte loads per lane issued before any is consumed
+constexpr uint32_t kNeverXor = 0x9e3779b9u;
+
+// A "piece" is 256 bytes of one row: 16 lanes x 16 bytes.  Wave w of W takes
+// pieces [w P / W, (w + 1) P / W) of the P = rows * row_bytes / 256 pieces; its
+// four 16-lane groups take consecutive pieces.
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint8_t* __restrict__ buf, int64_t rows,
+                                                              int32_t pieces_per_row, int64_t stride,
+                                                              uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n_waves = int64_t(gridDim.x) * (kThreads / 64);
+  const int64_t wave = int64_t(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
+  const int64_t pieces = rows * pieces_per_row;
+  const int64_t p0 = wave * pieces / n_waves, p1 = (wave + 1) * pieces / n_waves;
+  uint32_t acc = 0;
+  for (int64_t base = p0; base < p1; base += 4 * kLoadsInFlight) {
+    u32x4 v[kLoadsInFlight];
+#pragma unroll
+    for (int k = 0; k < kLoadsInFlight; ++k) {
+      const int64_t pc = base + 4 * k + lane / 16;
+      if (pc < p1) {
+        const int64_t r = pc / pieces_per_row, c = pc - r * pieces_per_row;
+        const u32x4* src = reinterpret_cast<const u32x4*>(buf + r * stride + c * 256 + (lane & 15) * 16);
+        v[k] = NT ? __builtin_nontemporal_load(src) : *src;
+      } else {
+        v[k] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kLoadsInFlight; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  if (acc == kNeverXor) sink[0] = acc;
+}
+
+template <int CH>
+__global__ __launch_bounds__(kThreads) void mfma_bf16_kernel(int32_t iters, float* sink) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(float(threadIdx.x & 7) * 0.125f);
+    b[i] = static_cast<__bf16>(float(i) * -0.25f);
+  }
+  f32x16 c[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) c[k] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < CH; ++k) s += c[k][0] + c[k][15];
+  if (s == 1.2345e30f) sink[0] = s;
+}
+
+}  // namespace
+
+extern "C" int kvc_ceiling_stream_read(const void* buf, int64_t rows, int32_t row_bytes, int64_t stride_bytes,
+                                       int32_t nontemporal, int32_t workgroups, uint32_t* sink,
+                                       hipStream_t stream) {
+  if (!buf || !sink || rows < 1 || row_bytes < 256 || row_bytes % 256 != 0 || stride_bytes < row_bytes ||
+      stride_bytes % 16 != 0 || workgroups < 1 || (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+    return -1;
+  const uint8_t* p = static_cast<const uint8_t*>(buf);
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3(workgroups), dim3(kThreads), 0, stream, p, rows,
+                       row_bytes / 256, stride_bytes, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3(workgroups), dim3(kThreads), 0, stream, p, rows,
+                       row_bytes / 256, stride_bytes, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" int kvc_ceiling_mfma_bf16(int32_t iters, int32_t chains, int32_t workgroups, float* sink,
+                                     hipStream_t stream) {
+  if (!sink || iters < 1 || workgroups < 1 || (chains != 2 && chains != 4)) return -1;
+  if (chains == 2)
+    hipLaunchKernelGGL(mfma_bf16_kernel<2>, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+  else
+    hipLaunchKernelGGL(mfma_bf16_kernel<4>, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}

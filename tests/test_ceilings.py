@@ -1,0 +1,96 @@
+"""The measured-ceiling probes (kv_cache_attention_kvcache_amd.ceilings).
+
+CPU: the separate library loads, exports exactly what ceilings.h declares,
+and rejects bad arguments before any launch.  GPU: the probes' rates are
+physically plausible for one MI355X (below the published peaks, well above
+what a broken probe would give), and the streaming read's byte count follows
+its row shape.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CEIL_DIR = os.path.join(ROOT, "kv_cache_attention_kvcache_amd", "ceilings")
+LIB = os.path.join(CEIL_DIR, "libkvc_ceilings.so")
+HEADER = os.path.join(CEIL_DIR, "ceilings.h")
+
+
+@pytest.fixture(scope="module")
+def ceil():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+
+        __graft_entry__._build_module().build()
+    from kv_cache_attention_kvcache_amd import ceilings
+
+    return ceilings
+
+
+def _declared():
+    return sorted(set(re.findall(r"^\s*int\s+(kvc_\w+)\s*\(", open(HEADER).read(), re.M)))
+
+
+def test_exports_match_header(ceil):
+    assert _declared() == sorted(ceil.EXPORTS)
+    raw = ctypes.CDLL(LIB)
+    for name in _declared():
+        assert hasattr(raw, name), name
+
+
+def test_libkvc_does_not_export_the_probes():
+    import kv_cache_attention_kvcache_amd as kvc
+
+    raw = ctypes.CDLL(kvc.LIB_PATH)
+    for name in _declared():
+        assert not hasattr(raw, name), name
+
+
+@pytest.mark.parametrize("rows,row,stride,wg", [
+    (0, 256, 256, 1),      # no rows
+    (4, 128, 256, 1),      # row not a multiple of 256 bytes
+    (4, 512, 256, 1),      # row longer than its stride
+    (4, 256, 264, 1),      # stride not 16-byte aligned
+    (4, 256, 256, 0),      # no workgroups
+])
+def test_stream_read_rejects_bad_shapes(ceil, rows, row, stride, wg):
+    lib = ceil._load()
+    rc = lib.kvc_ceiling_stream_read(ctypes.c_void_p(0x10000), rows, row, stride, 0, wg,
+                                     ctypes.c_void_p(0x20000), None)
+    assert rc == -1
+
+
+def test_null_and_misaligned_pointers_rejected(ceil):
+    lib = ceil._load()
+    assert lib.kvc_ceiling_stream_read(None, 4, 256, 256, 0, 1, ctypes.c_void_p(0x20000), None) == -1
+    assert lib.kvc_ceiling_stream_read(ctypes.c_void_p(0x10008), 4, 256, 256, 0, 1,
+                                       ctypes.c_void_p(0x20000), None) == -1
+    assert lib.kvc_ceiling_stream_read(ctypes.c_void_p(0x10000), 4, 256, 256, 0, 1, None, None) == -1
+    assert lib.kvc_ceiling_mfma_bf16(10, 2, 1, None, None) == -1
+    assert lib.kvc_ceiling_mfma_bf16(0, 2, 1, ctypes.c_void_p(0x20000), None) == -1
+    assert lib.kvc_ceiling_mfma_bf16(10, 3, 1, ctypes.c_void_p(0x20000), None) == -1
+
+
+@pytest.mark.gpu
+def test_measured_ceilings_are_plausible(ceil):
+    import torch
+
+    assert torch.cuda.is_available()
+    c = ceil.measure(buffer_gib=2, reps=3)
+    assert 3000 < c["hbm_read_gbps"]["value"] < 8000
+    assert 3000 < c["hbm_read_rows_gbps"]["value"] < 8000
+    assert 1500 < c["mfma_bf16_tflops"]["value"] < 2500
+
+
+@pytest.mark.gpu
+def test_stream_read_counts_row_bytes(ceil):
+    import torch
+
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    assert ceil.stream_read(buf, 256, 2048, True, 8, sink) == (1 << 20) // 8
+    assert ceil.stream_read(buf, 512, 512, False, 8, sink) == 1 << 20
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0  # zeros fold to an XOR of 0, which never matches the sentinel
