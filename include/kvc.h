@@ -40,7 +40,9 @@
  * Section 5.5 (Table 6): the KV cache can be kept in 8 bits, which halves the
  * bytes decode must stream.  K and V then hold int8 codes, and k_scale /
  * v_scale hold one float32 scale per cached vector, shape
- *     (n_layers, batch, max_seq, n_kv_heads).
+ *     (n_layers, batch, n_kv_heads, max_seq),
+ * head-major, so that one KV head's scales are contiguous over positions and
+ * a decode tile's scales are one dense run.
  * A vector x (the head_dim values of one position and KV head, as a bfloat16
  * cache would hold them: the rotated key rounded to bfloat16, the value
  * rounded to bfloat16) is stored as s = amax|x| / 127 and codes
@@ -101,7 +103,7 @@ typedef struct kvc_cache {
   int32_t n_kv_heads;
   int32_t head_dim;
   int32_t dtype;    /* KVC_F32, KVC_BF16 or KVC_I8 */
-  float* k_scale;   /* KVC_I8 only: device, (n_layers, batch, max_seq, n_kv_heads); else ignored */
+  float* k_scale;   /* KVC_I8 only: device, (n_layers, batch, n_kv_heads, max_seq); else ignored */
   float* v_scale;   /* KVC_I8 only: device, same shape */
   int32_t rolling;  /* 0: linear cache; 1: rolling window of max_seq positions (see below) */
 } kvc_cache;

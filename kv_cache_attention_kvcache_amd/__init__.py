@@ -95,13 +95,20 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def scale_shape(cache_shape):
+    """Shape of an int8 cache's k_scale / v_scale for a (n_layers, batch, max_seq, n_kv_heads, head_dim)
+    cache: (n_layers, batch, n_kv_heads, max_seq), head-major."""
+    n_layers, batch, max_seq, n_kv_heads = (int(x) for x in tuple(cache_shape)[:4])
+    return (n_layers, batch, n_kv_heads, max_seq)
+
+
 class KVCache:
     """A cache whose buffers are caller-owned torch tensors.
 
     k, v: (n_layers, batch, max_seq, n_kv_heads, head_dim), float32,
     bfloat16 or int8 (codes), contiguous, on one GPU; seqlens: (batch,) int32
     on that GPU.  An int8 cache also takes k_scale, v_scale: float32
-    (n_layers, batch, max_seq, n_kv_heads), one scale per cached vector; its
+    (n_layers, batch, n_kv_heads, max_seq), one scale per cached vector; its
     queries and outputs are bfloat16.  rolling=True keeps a window of the last
     max_seq positions: position p in slot p mod max_seq, seqlens counting every
     token seen.
@@ -117,10 +124,10 @@ class KVCache:
             raise ValueError("seqlens must be an int32 (batch,) device tensor")
         if k.dtype == torch.int8:
             for sc in (k_scale, v_scale):
-                if sc is None or sc.dtype != torch.float32 or tuple(sc.shape) != tuple(k.shape[:4]) \
+                if sc is None or sc.dtype != torch.float32 or tuple(sc.shape) != scale_shape(k.shape) \
                         or not sc.is_contiguous() or sc.device != k.device:
                     raise ValueError("an int8 cache needs contiguous float32 k_scale and v_scale of shape "
-                                     "(n_layers, batch, max_seq, n_kv_heads) on its device")
+                                     "(n_layers, batch, n_kv_heads, max_seq) on its device")
         self.k, self.v, self.seqlens = k, v, seqlens
         self.k_scale, self.v_scale = (k_scale, v_scale) if k.dtype == torch.int8 else (None, None)
         self._desc = kvc_cache(k.data_ptr(), v.data_ptr(), seqlens.data_ptr(), *[int(s) for s in k.shape],
@@ -133,8 +140,9 @@ class KVCache:
     def empty(cls, n_layers, batch, max_seq, n_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda",
               rolling: bool = False):
         shape = (n_layers, batch, max_seq, n_kv_heads, head_dim)
-        scales = (torch.zeros(shape[:4], dtype=torch.float32, device=device),
-                  torch.zeros(shape[:4], dtype=torch.float32, device=device)) if dtype == torch.int8 else (None, None)
+        scales = (torch.zeros(scale_shape(shape), dtype=torch.float32, device=device),
+                  torch.zeros(scale_shape(shape), dtype=torch.float32, device=device)) \
+            if dtype == torch.int8 else (None, None)
         return cls(torch.empty(shape, dtype=dtype, device=device), torch.empty(shape, dtype=dtype, device=device),
                    torch.zeros(batch, dtype=torch.int32, device=device), *scales, rolling=rolling)
 

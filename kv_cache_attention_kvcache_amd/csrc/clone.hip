@@ -7,8 +7,9 @@
 // row (read once, write N times: HBM-bound).  A second, one-workgroup kernel
 // then sets the destination lengths, so no block reads a length another
 // block may already have changed.  An int8 cache also has one float32 scale
-// per (position, KV head) for K and for V; those runs are copied the same way
-// (grid planes 2 and 3), 4 bytes at a time.
+// per (KV head, position) for K and for V, head-major: per layer, each KV
+// head's positions [0, src_len) are one run, copied the same way (grid planes
+// 2 and 3), 4 bytes at a time.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 #include "kvc.h"
@@ -24,15 +25,15 @@ __global__ __launch_bounds__(256) void clone_copy_kernel(CloneParams p) {
   const int layer = blockIdx.y;
   const int n_rows = p.dst.batch;
   if (blockIdx.z >= 2) {  // scales of an int8 cache
-    const size_t n = size_t(p.src_len) * p.src.n_kv_heads;
-    const float* src = (blockIdx.z == 2 ? p.src.k_scale : p.src.v_scale) +
-                       size_t(layer) * p.src.max_seq * p.src.n_kv_heads;
+    const int hkv = p.src.n_kv_heads;
+    const size_t n = size_t(p.src_len) * hkv;
+    const float* src = (blockIdx.z == 2 ? p.src.k_scale : p.src.v_scale) + size_t(layer) * hkv * p.src.max_seq;
     float* dst0 = blockIdx.z == 2 ? p.dst.k_scale : p.dst.v_scale;
-    const size_t dst_row = size_t(p.dst.max_seq) * p.dst.n_kv_heads;
     for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x) {
-      const float val = src[i];
+      const size_t h = i / p.src_len, pos = i - h * p.src_len;
+      const float val = src[h * p.src.max_seq + pos];
       for (int r = 0; r < n_rows; ++r)
-        if (p.dst.seqlens[r] == 0) dst0[(size_t(layer) * n_rows + r) * dst_row + i] = val;
+        if (p.dst.seqlens[r] == 0) dst0[((size_t(layer) * n_rows + r) * hkv + h) * p.dst.max_seq + pos] = val;
     }
     return;
   }

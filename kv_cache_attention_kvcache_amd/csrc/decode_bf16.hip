@@ -268,11 +268,11 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
   int off_keep = 0;
 #pragma unroll
   for (int k = C::HB; k < C::S; ++k) off_keep += ((x >> (C::S - 1 - k)) & 1) * ((C::NR >> (k - C::HB)) / 2);
-  int sc_off[C::NRK];  // byte offset of kept row r's scale within a tile's scale run
+  int sc_off[C::NRK];  // byte offset of kept row r's scale within a tile's (dense) scale run
 #pragma unroll
   for (int r = 0; r < C::NRK; ++r) {
     const int slot = r + off_keep;
-    sc_off[r] = (2 * ((slot >> 1) * C::RPI + rg) + (slot & 1)) * hkv * 4;
+    sc_off[r] = (2 * ((slot >> 1) * C::RPI + rg) + (slot & 1)) * 4;
   }
 
   SegPos seg = find_segment(p, t_begin, lane);
@@ -291,8 +291,9 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
     const size_t vec0 = size_t(seg.b) * p.kv.max_seq * hkv + g;
     const uint8_t* kseg = static_cast<const uint8_t*>(p.kv.k) + vec0 * D * E::kBytes;
     const uint8_t* vseg = static_cast<const uint8_t*>(p.kv.v) + vec0 * D * E::kBytes;
-    const float* ksseg = Q8 ? p.kv.k_scale + vec0 : nullptr;
-    const float* vsseg = Q8 ? p.kv.v_scale + vec0 : nullptr;
+    const size_t sc0 = (size_t(seg.b) * hkv + g) * p.kv.max_seq;  // scales are head-major
+    const float* ksseg = Q8 ? p.kv.k_scale + sc0 : nullptr;
+    const float* vsseg = Q8 ? p.kv.v_scale + sc0 : nullptr;
 
     // Queries of this block in this lane's head order: slot h holds head h ^ gh(x), dims [8x, 8x+8).
     u32x4_t q[GB];
@@ -332,9 +333,9 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
     auto issue_sc = [&](const float* base, int j, float* buf) {
       if constexpr (Q8) {
         const int key0 = j * kTileKeys;
-        const int left = (L - key0 - 1) * hkv * 4 + 4;
+        const int left = (L - key0) * 4;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(base) + size_t(key0) * hkv, (short)0, left > 0 ? left : 0, kRsrcWord3);
+            const_cast<float*>(base) + key0, (short)0, left > 0 ? left : 0, kRsrcWord3);
 #pragma unroll
         for (int i = 0; i < C::NRK; ++i)
           buf[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, sc_off[i], 0, kCpolNT));
@@ -599,10 +600,14 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
 //     unscaled probability.  Lazy running max per head as in the vector path.
 //   * V^T in LDS as bfloat16 key pairs per head dim; O^T += V^T P^T.
 constexpr int kQ8Cols = kDecodeQ8Block;  // query heads per segment (MFMA columns)
+// Tiles whose loads are in flight per wave.  One streams fastest: the K loads take 32 bytes
+// of 32 rows each, and a second tile's worth of such partial-row requests slows the memory
+// side more than it hides latency (measured at 72K context: 272 us against 282-285 us at
+// batch 8; three tiles no longer fit the registers).
 #ifndef KVC_Q8_STAGES
-#define KVC_Q8_STAGES 2
+#define KVC_Q8_STAGES 1
 #endif
-constexpr int kQ8Stages = KVC_Q8_STAGES;  // tiles in flight per wave
+constexpr int kQ8Stages = KVC_Q8_STAGES;
 
 // Tile row fed as A-operand row i so that output register r of lane (column,
 // half h) holds key 16 (r >> 3) + 8 h + (r & 7).
@@ -666,8 +671,9 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_q8_mfma_kernel(Decod
     const size_t vec0 = size_t(seg.b) * p.kv.max_seq * hkv + g;
     const uint8_t* kseg = static_cast<const uint8_t*>(p.kv.k) + vec0 * D;
     const uint8_t* vseg = static_cast<const uint8_t*>(p.kv.v) + vec0 * D;
-    const float* ksseg = p.kv.k_scale + vec0;
-    const float* vsseg = p.kv.v_scale + vec0;
+    const size_t sc0 = (size_t(seg.b) * hkv + g) * p.kv.max_seq;  // scales are head-major
+    const float* ksseg = p.kv.k_scale + sc0;
+    const float* vsseg = p.kv.v_scale + sc0;
 
     // Q^T B operands: lane (column = query head l32 of the group, half): head
     // dims 32m + 16 half + 8e .. +8 at k-step 2m + e; zero for padding heads.
@@ -716,10 +722,10 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_q8_mfma_kernel(Decod
         st.v[it][0] = __builtin_amdgcn_raw_buffer_load_b128(rv, 2 * kp * row_bytes + 16 * dg, 0, 0);
         st.v[it][1] = __builtin_amdgcn_raw_buffer_load_b128(rv, (2 * kp + 1) * row_bytes + 16 * dg, 0, 0);
       }
-      const __amdgpu_buffer_rsrc_t rks = rsrc_at(ksseg, j, 4, hkv * 4);
-      const __amdgpu_buffer_rsrc_t rvs = rsrc_at(vsseg, j, 4, hkv * 4);
-      st.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, l32 * hkv * 4, 0, kCpolNT));
-      st.vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, l32 * hkv * 4, 0, kCpolNT));
+      const __amdgpu_buffer_rsrc_t rks = rsrc_at(ksseg, j, 4, 4);
+      const __amdgpu_buffer_rsrc_t rvs = rsrc_at(vsseg, j, 4, 4);
+      st.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, l32 * 4, 0, kCpolNT));
+      st.vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, l32 * 4, 0, kCpolNT));
     };
     auto process = [&](int j, Stage& st, int j_next) {
       // ---- V^T key pairs and the scales into the wave's LDS (the last tile's reads are done)
@@ -807,8 +813,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_q8_mfma_kernel(Decod
         }
     };
 
-    // The wave's tiles of this run: j0 + wave, j0 + wave + 4, ...; kQ8Stages tiles in flight
-    // (one wave per SIMD: the bytes in flight, not the ALUs, set the streaming rate).
+    // The wave's tiles of this run: j0 + wave, j0 + wave + 4, ...; kQ8Stages tiles in flight.
     Stage st[kQ8Stages];
     int j = j0 + wave;
 #pragma unroll

@@ -15,7 +15,7 @@ struct LayerView {
   void* v;
   const int32_t* seqlens;
   int32_t batch, max_seq, n_kv_heads, head_dim, dtype;
-  float* k_scale;  // int8 caches: (batch, max_seq, n_kv_heads) scales of this layer; else null
+  float* k_scale;  // int8 caches: (batch, n_kv_heads, max_seq) scales of this layer; else null
   float* v_scale;
   int32_t rolling;  // rolling window: position p in slot p mod max_seq
 };

@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256) void rope_append_q8_kernel(RopeAppendParams p)
 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const size_t vec0 = (size_t(b) * p.kv.max_seq + slot_of(p.kv, pos)) * hkv;  // this slot's first (head) vector
+  const int slot = slot_of(p.kv, pos);
+  const size_t vec0 = (size_t(b) * p.kv.max_seq + slot) * hkv;  // this slot's first (head) vector
   for (int vi = wave; vi < 2 * hkv; vi += blockDim.x / kWave) {
     const bool is_k = vi < hkv;
     const int g = is_k ? vi : vi - hkv;
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(256) void rope_append_q8_kernel(RopeAppendParams p)
       const float c = sc > 0.f ? fminf(fmaxf(rintf(x[u] / sc), -127.f), 127.f) : 0.f;
       dst[lane + kWave * u] = static_cast<int8_t>(c);
     }
-    if (lane == 0) (is_k ? p.kv.k_scale : p.kv.v_scale)[vec0 + g] = sc;
+    if (lane == 0) (is_k ? p.kv.k_scale : p.kv.v_scale)[(size_t(b) * hkv + g) * p.kv.max_seq + slot] = sc;
   }
 }
 

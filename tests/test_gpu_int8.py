@@ -23,8 +23,8 @@ def _int8_cache(kvc, n_layers, batch, max_seq, hkv, d, poison=True):
     shape = (n_layers, batch, max_seq, hkv, d)
     k = torch.full(shape, 0x55 if poison else 0, dtype=torch.int8, device="cuda")
     v = torch.full(shape, 0x55 if poison else 0, dtype=torch.int8, device="cuda")
-    ks = torch.full(shape[:4], float("nan") if poison else 0.0, dtype=torch.float32, device="cuda")
-    vs = torch.full(shape[:4], float("nan") if poison else 0.0, dtype=torch.float32, device="cuda")
+    ks = torch.full(kvc.scale_shape(shape), float("nan") if poison else 0.0, dtype=torch.float32, device="cuda")
+    vs = torch.full(kvc.scale_shape(shape), float("nan") if poison else 0.0, dtype=torch.float32, device="cuda")
     return kvc.KVCache(k, v, torch.zeros(batch, dtype=torch.int32, device="cuda"), ks, vs)
 
 
@@ -40,8 +40,8 @@ def _fill_int8_prefix(cache, layer, lengths, g):
         if n:
             cache.k[layer, b, :n] = torch.from_numpy(kc).cuda()
             cache.v[layer, b, :n] = torch.from_numpy(vc).cuda()
-            cache.k_scale[layer, b, :n] = torch.from_numpy(ks).cuda()
-            cache.v_scale[layer, b, :n] = torch.from_numpy(vs).cuda()
+            cache.k_scale[layer, b, :, :n] = torch.from_numpy(np.ascontiguousarray(ks.T)).cuda()  # head-major
+            cache.v_scale[layer, b, :, :n] = torch.from_numpy(np.ascontiguousarray(vs.T)).cuda()
         hist.append((kc, ks, vc, vs))
     cache.seqlens.copy_(torch.tensor(lengths, dtype=torch.int32))
     return hist
@@ -70,7 +70,9 @@ def test_int8_append_stores_the_oracle_codes_and_scales(kvc, hq, hkv, d, t_len):
     torch.cuda.synchronize()
     assert torch.equal(q_out.view(torch.int16), q_ref.view(torch.int16))
     kc_all, vc_all = cache.k.cpu().numpy(), cache.v.cpu().numpy()
-    ks_all, vs_all = cache.k_scale.cpu().numpy(), cache.v_scale.cpu().numpy()
+    # scales are stored head-major; compare them in the codes' (layer, row, position, head) order
+    ks_all = cache.k_scale.cpu().numpy().transpose(0, 1, 3, 2)
+    vs_all = cache.v_scale.cpu().numpy().transpose(0, 1, 3, 2)
     touched = np.zeros(kc_all.shape[:4], dtype=bool)
     k_bf16 = host64(ref_cache.k)  # the rotated, bfloat16-rounded keys (bytes shared with the int8 append)
     for b, p in enumerate(starts):
@@ -146,14 +148,15 @@ def test_int8_clone_copies_codes_and_scales(kvc):
     torch.cuda.synchronize()
     assert err.item() == 0
     assert torch.equal(dst.seqlens.cpu(), torch.full((4,), n, dtype=torch.int32))
-    for t_src, t_dst in ((src.k, dst.k), (src.v, dst.v), (src.k_scale, dst.k_scale), (src.v_scale, dst.v_scale)):
-        a = t_src[:, 0, :n].cpu()
-        a = a.view(torch.int32) if a.dtype == torch.float32 else a  # compare scale bits
+    for t_src, t_dst in ((src.k, dst.k), (src.v, dst.v)):
         for r in range(4):
-            bb = t_dst[:, r, :n].cpu()
-            assert torch.equal(bb.view(torch.int32) if bb.dtype == torch.float32 else bb, a)
+            assert torch.equal(t_dst[:, r, :n].cpu(), t_src[:, 0, :n].cpu())
+    for t_src, t_dst in ((src.k_scale, dst.k_scale), (src.v_scale, dst.v_scale)):  # head-major: positions last
+        for r in range(4):
+            assert torch.equal(t_dst[:, r, :, :n].cpu().view(torch.int32), t_src[:, 0, :, :n].cpu().view(torch.int32))
     # positions at or past n keep their poison
-    assert torch.all(dst.k[:, :, n:].cpu() == 0x55) and torch.all(torch.isnan(dst.k_scale[:, :, n:].cpu()))
+    assert torch.all(dst.k[:, :, n:].cpu() == 0x55) and torch.all(torch.isnan(dst.k_scale[:, :, :, n:].cpu()))
+    assert torch.all(torch.isnan(dst.v_scale[:, :, :, n:].cpu()))
 
 
 def test_int8_cache_rejected_by_prefill_and_decode_step(kvc):

@@ -48,8 +48,8 @@ def _ring(kvc, path, dtype, hq, hkv, d, seed):
             vc, vs = quant.quantize_int8(v_hat)
             cache.k[0, b, slots] = torch.from_numpy(kc).cuda()
             cache.v[0, b, slots] = torch.from_numpy(vc).cuda()
-            cache.k_scale[0, b, slots] = torch.from_numpy(ks).cuda()
-            cache.v_scale[0, b, slots] = torch.from_numpy(vs).cuda()
+            cache.k_scale[0, b][:, slots] = torch.from_numpy(np.ascontiguousarray(ks.T)).cuda()  # head-major
+            cache.v_scale[0, b][:, slots] = torch.from_numpy(np.ascontiguousarray(vs.T)).cuda()
         else:
             cache.k[0, b, slots] = dev(k_hat, dtype)
             cache.v[0, b, slots] = dev(v_hat, dtype)
