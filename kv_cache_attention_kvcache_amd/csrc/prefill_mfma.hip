@@ -70,12 +70,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
   const int hkv = p.kv.n_kv_heads;
   const int group = hq / hkv;
   const int n_qt = (p.T + kBM - 1) / kBM;
-  const int n_wg = n_qt * hq * p.kv.batch;
-  // XCD-aware order: consecutive logical ids land on one XCD.
+  // XCD-aware order.  Workgroup x runs on XCD x mod 8, and each XCD starts its
+  // workgroups in the order of x / 8.  When the (row, head) pairs split evenly
+  // over the 8 XCDs, XCD i takes the consecutive pairs [i rpx, (i + 1) rpx) --
+  // the query heads of one KV head, which share its K/V stream through that
+  // XCD's L2 -- and starts all their latest (longest) query tiles first, then
+  // the next latest, and so on.  Otherwise workgroups go in plain order.
   const int x = blockIdx.x;
-  const int lid = (n_wg % 8 == 0) ? (x % 8) * (n_wg / 8) + x / 8 : x;
-  const int qt = n_qt - 1 - lid % n_qt;  // latest tiles first
-  const int rest = lid / n_qt;
+  int qt, rest;
+  if ((hq * p.kv.batch) % 8 == 0) {
+    const int rpx = hq * p.kv.batch / 8;  // (row, head) pairs per XCD
+    const int j = x / 8;                  // start order within the XCD
+    qt = n_qt - 1 - j / rpx;
+    rest = (x % 8) * rpx + j % rpx;
+  } else {
+    qt = n_qt - 1 - x % n_qt;
+    rest = x / n_qt;
+  }
   const int h = rest % hq;
   const int b = rest / hq;
   const int g = h / group;
