@@ -89,7 +89,8 @@ enum {
 enum {
   KVC_DEV_CAPACITY = 1,  /* seqlens[b] < 0, or seqlens[b] + T > max_seq: row b skipped */
   KVC_DEV_NOT_EMPTY = 2, /* clone: destination row b had seqlens[b] != 0: row b skipped */
-  KVC_DEV_SRC_LEN = 4    /* clone: source seqlens[0] != src_len: nothing copied */
+  KVC_DEV_SRC_LEN = 4,   /* clone: source seqlens[0] != src_len: nothing copied */
+  KVC_DEV_TOKENS = 8     /* ragged calls: row b's token range in cu_tokens is malformed: row b skipped */
 };
 
 /* Describes caller-owned device buffers; the library only reads the struct. */
@@ -198,6 +199,62 @@ int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, vo
  */
 int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out,
                      int32_t T, int32_t n_q_heads, float scale, int32_t* dev_err, void* stream);
+
+/*
+ * Ragged batches.  Cake paper, Section 3: serving systems run chunked prefill
+ * beside decoding in one batch (the chunk of one request next to the single
+ * new tokens of others).  The two calls below take such a batch: row b brings
+ * T_b >= 0 new tokens, packed one after another,
+ *
+ *   cu_tokens   device int32, (batch + 1,): row b's tokens are packed rows
+ *               [cu_tokens[b], cu_tokens[b+1]) of q, q_out, k_new, v_new and
+ *               out; T_b = cu_tokens[b+1] - cu_tokens[b].  Read, never written.
+ *   n_tokens    packed rows in those tensors (their leading dimension), >= 0.
+ *   max_tokens  host-known bound on every T_b, >= 1; it sizes the grid.
+ *
+ * and the tensors are (n_tokens, heads, head_dim).  A row whose range is
+ * malformed (cu_tokens[b] < 0, a decreasing pair, an end past n_tokens, or
+ * T_b > max_tokens) is skipped and KVC_DEV_TOKENS is set; nothing outside the
+ * packed rows is ever read or written.  A row with T_b = 0 is left alone.
+ * Otherwise each row follows the rules of the uniform calls with T = T_b.
+ */
+
+/*
+ * kvc_rope_append_ragged -- kvc_rope_append for a ragged batch: row b's T_b
+ * tokens go to positions P .. P + T_b - 1 (P = seqlens[b]), its rotated
+ * queries to the same packed rows of q_out.  Rows with P < 0 or
+ * P + T_b > max_seq are skipped (KVC_DEV_CAPACITY); on a rolling cache
+ * max_tokens must not exceed max_seq.
+ */
+int kvc_rope_append_ragged(const kvc_cache* cache, int32_t layer, const void* q, void* q_out,
+                           const void* k_new, const void* v_new, const int32_t* cu_tokens,
+                           int32_t n_tokens, int32_t max_tokens, int32_t n_q_heads, float rope_base,
+                           int32_t* dev_err, void* stream);
+
+/*
+ * kvc_attn_mixed -- attention for a ragged batch in one call, after its k/v
+ * were appended: rows with one new token decode (keys 0..P, as
+ * kvc_attn_decode, the rolling rule included), rows with more prefill
+ * causally (query t sees keys 0..P+t, as kvc_attn_prefill, linear rule),
+ * rows with none are left alone.
+ *
+ *   q_rot, out  device, (n_tokens, n_q_heads, head_dim), packed.
+ *   scale, n_workers, workspace, workspace_bytes  as kvc_attn_decode: the
+ *               workspace needs kvc_decode_workspace_bytes(cache, n_q_heads,
+ *               n_workers) bytes (none for float32 caches).
+ *
+ * bfloat16: the prefill rows run the matrix-core prefill kernel and the
+ * decode rows the split-KV decode (two launches and the fold, in stream
+ * order; each kernel skips the other's rows).  float32: one launch, one
+ * direct split per query row.  int8 caches are rejected (KVC_E_DTYPE), as by
+ * kvc_attn_prefill.  The outputs of a prefill row are bit-identical to
+ * kvc_attn_prefill on that row alone; a decode row's differ from
+ * kvc_attn_decode only in the order of float32 additions.
+ */
+int kvc_attn_mixed(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out,
+                   const int32_t* cu_tokens, int32_t n_tokens, int32_t max_tokens, int32_t n_q_heads,
+                   float scale, int32_t n_workers, void* workspace, size_t workspace_bytes,
+                   int32_t* dev_err, void* stream);
 
 /*
  * kvc_decode_step -- one decode token per row in a single launch: RoPE of the

@@ -31,9 +31,10 @@ KVC_E_LAUNCH = -6
 KVC_DEV_CAPACITY = 1
 KVC_DEV_NOT_EMPTY = 2
 KVC_DEV_SRC_LEN = 4
+KVC_DEV_TOKENS = 8
 
-EXPORTS = ("kvc_rope_append", "kvc_decode_workspace_bytes", "kvc_attn_decode", "kvc_attn_prefill",
-           "kvc_decode_step", "kvc_prefill_clone", "kvc_status_string")
+EXPORTS = ("kvc_rope_append", "kvc_rope_append_ragged", "kvc_decode_workspace_bytes", "kvc_attn_decode",
+           "kvc_attn_prefill", "kvc_attn_mixed", "kvc_decode_step", "kvc_prefill_clone", "kvc_status_string")
 
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16, torch.int8: KVC_I8}
 
@@ -53,6 +54,10 @@ def _load():
     cp = ctypes.POINTER(kvc_cache)
     lib.kvc_rope_append.argtypes = [cp, I32, P, P, P, P, I32, I32, F32, P, P]
     lib.kvc_rope_append.restype = ctypes.c_int
+    lib.kvc_rope_append_ragged.argtypes = [cp, I32, P, P, P, P, P, I32, I32, I32, F32, P, P]
+    lib.kvc_rope_append_ragged.restype = ctypes.c_int
+    lib.kvc_attn_mixed.argtypes = [cp, I32, P, P, P, I32, I32, I32, F32, I32, P, SZ, P, P]
+    lib.kvc_attn_mixed.restype = ctypes.c_int
     lib.kvc_decode_workspace_bytes.argtypes = [cp, I32, I32]
     lib.kvc_decode_workspace_bytes.restype = SZ
     lib.kvc_attn_decode.argtypes = [cp, I32, P, P, I32, F32, I32, P, SZ, P, P]
@@ -252,6 +257,71 @@ def kvc_decode_step(cache: KVCache, layer: int, q, k_new, v_new, out=None, scale
     st = lib.kvc_decode_step(cache.desc(), int(layer), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), int(hq),
                              float(scale), float(rope_base), _ptr(dev_err), _stream(stream, cache.k.device))
     _check("kvc_decode_step", st)
+    return out
+
+
+class RaggedBatch:
+    """The token layout of a ragged call: row b brings counts[b] new tokens, packed in row order.
+
+    cu_tokens is the (batch + 1,) int32 device prefix array the library reads; n_tokens and
+    max_tokens are the host-known total and bound the calls take."""
+
+    def __init__(self, counts, device="cuda"):
+        counts = [int(c) for c in counts]
+        if any(c < 0 for c in counts):
+            raise ValueError("token counts must be >= 0")
+        cu = [0]
+        for c in counts:
+            cu.append(cu[-1] + c)
+        self.counts = counts
+        self.n_tokens = cu[-1]
+        self.max_tokens = max(1, max(counts, default=0))
+        self.cu_tokens = torch.tensor(cu, dtype=torch.int32, device=device)
+
+    def first(self, b: int) -> int:
+        """Packed row of row b's first token."""
+        return sum(self.counts[:b])
+
+
+def kvc_rope_append_ragged(cache: KVCache, layer: int, q, k_new, v_new, rb: RaggedBatch, q_out=None,
+                           rope_base: float = 10000.0, dev_err=None, stream=None):
+    """kvc_rope_append for a ragged batch: q (n_tokens, Hq, D), k_new/v_new (n_tokens, Hkv, D),
+    row b's tokens at the packed rows rb gives it; returns q_out."""
+    n, hq, d = q.shape
+    _like(q, cache, (rb.n_tokens, hq, cache.head_dim), "q")
+    _like(k_new, cache, (rb.n_tokens, cache.n_kv_heads, cache.head_dim), "k_new")
+    _like(v_new, cache, (rb.n_tokens, cache.n_kv_heads, cache.head_dim), "v_new")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _like(q_out, cache, q.shape, "q_out")
+    if rb.cu_tokens.numel() != cache.batch + 1 or rb.cu_tokens.device != cache.k.device:
+        raise ValueError("the ragged batch must have batch + 1 prefix entries on the cache's device")
+    st = lib.kvc_rope_append_ragged(cache.desc(), int(layer), _ptr(q), _ptr(q_out), _ptr(k_new), _ptr(v_new),
+                                    _ptr(rb.cu_tokens), int(rb.n_tokens), int(rb.max_tokens), int(hq),
+                                    float(rope_base), _ptr(dev_err), _stream(stream, cache.k.device))
+    _check("kvc_rope_append_ragged", st)
+    return q_out
+
+
+def kvc_attn_mixed(cache: KVCache, layer: int, q_rot, rb: RaggedBatch, out=None, scale: float = 0.0,
+                   n_workers: int = 0, workspace=None, dev_err=None, stream=None):
+    """Attention for a ragged batch: one-token rows decode, longer rows prefill causally; q_rot and
+    out are (n_tokens, Hq, D), packed as rb says.  Returns out."""
+    n, hq, d = q_rot.shape
+    _like(q_rot, cache, (rb.n_tokens, hq, cache.head_dim), "q_rot")
+    if out is None:
+        out = torch.empty_like(q_rot)
+    _like(out, cache, q_rot.shape, "out")
+    if rb.cu_tokens.numel() != cache.batch + 1 or rb.cu_tokens.device != cache.k.device:
+        raise ValueError("the ragged batch must have batch + 1 prefix entries on the cache's device")
+    need = kvc_decode_workspace_bytes(cache, hq, n_workers)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=cache.k.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kvc_attn_mixed(cache.desc(), int(layer), _ptr(q_rot), _ptr(out), _ptr(rb.cu_tokens),
+                            int(rb.n_tokens), int(rb.max_tokens), int(hq), float(scale), int(n_workers),
+                            _ptr(workspace), ws_bytes, _ptr(dev_err), _stream(stream, cache.k.device))
+    _check("kvc_attn_mixed", st)
     return out
 
 

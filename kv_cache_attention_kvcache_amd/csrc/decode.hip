@@ -74,8 +74,15 @@ __global__ __launch_bounds__(256, 1) void split_attention_kernel(SplitParams p) 
   const int h0 = g * group + (hb_all - g * n_hb) * GB;
   const int b = row / p.T;
   const int t = row - b * p.T;
+  const RowTokens rt = row_tokens(p.kv, b, p.T);  // ragged calls: T = max_tokens
+  if (rt.count < 0) {
+    if (split == 0 && hb_all == 0 && t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_TOKENS);
+    return;
+  }
+  if (t >= rt.count || !row_selected(p.kv, rt.count)) return;
+  const size_t tok = size_t(rt.first) + t;  // packed row of this query and its output
 
-  const int n_keys = attended_keys(p.kv, p.kv.seqlens[b], p.T, t);  // keys 0 .. start + t
+  const int n_keys = attended_keys(p.kv, p.kv.seqlens[b], rt.count, t);  // keys 0 .. start + t
   if (n_keys < 0) {
     if (split == 0 && hb_all == 0 && t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
     return;
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(256, 1) void split_attention_kernel(SplitParams p) 
   // The query block is read-only for the whole kernel: address it as constant
   // memory so that its wave-uniform loads go through the scalar cache.
   const const_uint4_ptr q_vec = reinterpret_cast<const_uint4_ptr>(
-      reinterpret_cast<uintptr_t>(static_cast<const T*>(p.q) + (size_t(row) * p.n_q_heads + h0) * D));
+      reinterpret_cast<uintptr_t>(static_cast<const T*>(p.q) + (tok * p.n_q_heads + h0) * D));
 
   // Online-softmax state (log2 units); lpart is this lane's share of the sum.
   float m[GB], lpart[GB], acc[GB][C::kDimsPerLane];
@@ -299,11 +306,12 @@ __global__ __launch_bounds__(256, 1) void split_attention_kernel(SplitParams p) 
       o += f * red_o[(w * GB + h) * D + d];
       l += f * red_l[w * GB + h];
     }
-    const size_t qh = size_t(row) * p.n_q_heads + h0 + h;
+    const size_t qh = size_t(row) * p.n_q_heads + h0 + h;  // workspace slot of (row, head)
     if (p.direct || single) {
       const float y = o / l;
-      if constexpr (C::kBf16) static_cast<bf16_t*>(p.out)[qh * D + d] = f32_to_bf16(y);
-      else static_cast<float*>(p.out)[qh * D + d] = y;
+      const size_t oi = (tok * p.n_q_heads + h0 + h) * D + d;
+      if constexpr (C::kBf16) static_cast<bf16_t*>(p.out)[oi] = f32_to_bf16(y);
+      else static_cast<float*>(p.out)[oi] = y;
     } else {
       p.ws_o[(qh * p.max_splits + split) * D + d] = o;
       if (d == 0) {
@@ -318,11 +326,14 @@ __global__ __launch_bounds__(256, 1) void split_attention_kernel(SplitParams p) 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void split_combine_kernel(SplitParams p) {
   constexpr int kPer = D / kWave;
-  const int qh = blockIdx.x;  // row * Hq + h
+  const int qh = blockIdx.x;  // row * Hq + h: the workspace slot
   const int row = qh / p.n_q_heads;
   const int b = row / p.T;
   const int t = row - b * p.T;
-  const int n_keys = attended_keys(p.kv, p.kv.seqlens[b], p.T, t);
+  const RowTokens rt = row_tokens(p.kv, b, p.T);
+  if (t >= rt.count || !row_selected(p.kv, rt.count)) return;  // includes malformed rows (count -1)
+  const size_t oq = (size_t(rt.first) + t) * p.n_q_heads + (qh - row * p.n_q_heads);  // packed (token, head)
+  const int n_keys = attended_keys(p.kv, p.kv.seqlens[b], rt.count, t);
   if (n_keys < 0) return;
   const int n_split = (n_keys + p.split_keys - 1) / p.split_keys;
   if (n_split <= 1) return;  // written directly by the split pass
@@ -343,8 +354,8 @@ __global__ __launch_bounds__(64) void split_combine_kernel(SplitParams p) {
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int d = threadIdx.x + i * kWave;
-    if constexpr (sizeof(T) == 2) static_cast<bf16_t*>(p.out)[size_t(qh) * D + d] = f32_to_bf16(acc[i] * inv);
-    else static_cast<float*>(p.out)[size_t(qh) * D + d] = acc[i] * inv;
+    if constexpr (sizeof(T) == 2) static_cast<bf16_t*>(p.out)[oq * D + d] = f32_to_bf16(acc[i] * inv);
+    else static_cast<float*>(p.out)[oq * D + d] = acc[i] * inv;
   }
 }
 

@@ -165,8 +165,19 @@ struct Elem<true> {  // int8 codes: 8 bytes, widened exactly (|code| <= 127 fits
   }
 };
 
-// Keys row b's decode query attends (-1: out of range), and their 32-key tiles (0 if out of range).
-__device__ __forceinline__ int row_keys(const LayerView& kv, int b) { return attended_keys(kv, kv.seqlens[b], 1, 0); }
+// Keys row b's decode query attends, and their 32-key tiles (0 when negative):
+// -1 out of range (KVC_DEV_CAPACITY); -2 not in this launch (a ragged call's row
+// with no token or with a prefill chunk); -3 a malformed token range (KVC_DEV_TOKENS).
+__device__ __forceinline__ int row_keys(const LayerView& kv, int b) {
+  if (kv.cu_tokens) {
+    const RowTokens rt = row_tokens(kv, b, 1);
+    if (rt.count < 0) return -3;
+    if (rt.count != 1 || !row_selected(kv, rt.count)) return -2;
+  }
+  return attended_keys(kv, kv.seqlens[b], 1, 0);
+}
+// Packed row of row b's query and output (row b itself unless the call is ragged).
+__device__ __forceinline__ int row_token(const LayerView& kv, int b) { return kv.cu_tokens ? kv.cu_tokens[b] : b; }
 __device__ __forceinline__ int row_tiles(const LayerView& kv, int b) {
   const int n = row_keys(kv, b);
   return n < 0 ? 0 : (n + kTileKeys - 1) / kTileKeys;
@@ -298,7 +309,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
     // Queries of this block in this lane's head order: slot h holds head h ^ gh(x), dims [8x, 8x+8).
     u32x4_t q[GB];
     {
-      const bf16_t* qrow = static_cast<const bf16_t*>(p.q) + (size_t(seg.b) * hq + g * group + hb * GB) * D;
+      const bf16_t* qrow =
+          static_cast<const bf16_t*>(p.q) + (size_t(row_token(p.kv, seg.b)) * hq + g * group + hb * GB) * D;
 #pragma unroll
       for (int h = 0; h < GB; ++h) {
         const int head = h ^ ghx;
@@ -547,7 +559,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
       }
       if (complete) {
         if (hb * GB + h < group)
-          static_cast<bf16_t*>(p.out)[(size_t(seg.b) * hq + g * group + hb * GB + h) * D + d] = f32_to_bf16(o / l);
+          static_cast<bf16_t*>(p.out)[(size_t(row_token(p.kv, seg.b)) * hq + g * group + hb * GB + h) * D + d] =
+              f32_to_bf16(o / l);
       } else {
         const size_t ps = (size_t(blockIdx.x) * 2 + slot) * GB + h;
         p.ws_o[ps * D + d] = o;
@@ -680,7 +693,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_q8_mfma_kernel(Decod
     u32x4_t qb[kKD];
     {
       const bool valid = l32 < group;
-      const bf16_t* qrow = static_cast<const bf16_t*>(p.q) + (size_t(seg.b) * hq + g * group + (valid ? l32 : 0)) * D;
+      const bf16_t* qrow = static_cast<const bf16_t*>(p.q) +
+                           (size_t(row_token(p.kv, seg.b)) * hq + g * group + (valid ? l32 : 0)) * D;
 #pragma unroll
       for (int m = 0; m < kM; ++m)
 #pragma unroll
@@ -859,7 +873,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_q8_mfma_kernel(Decod
         l += f * red_ml[(w * GB + h) * 2 + 1];
       }
       if (complete) {
-        static_cast<bf16_t*>(p.out)[(size_t(seg.b) * hq + g * group + h) * D + d] = f32_to_bf16(ov / l);
+        static_cast<bf16_t*>(p.out)[(size_t(row_token(p.kv, seg.b)) * hq + g * group + h) * D + d] =
+            f32_to_bf16(ov / l);
       } else {
         const size_t ps = (size_t(blockIdx.x) * 2 + slot) * GB + h;
         p.ws_o[ps * D + d] = ov;
@@ -909,7 +924,11 @@ __global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p
 
   const int nt = row_tiles(p.kv, b);
   if (nt == 0) {
-    if (sr == 0 && h == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
+    if (sr == 0 && h == 0 && threadIdx.x == 0) {
+      const int why = row_keys(p.kv, b);
+      if (why == -1) report(p.dev_err, KVC_DEV_CAPACITY);
+      if (why == -3) report(p.dev_err, KVC_DEV_TOKENS);
+    }
     return;
   }
   if (hb * GB + h >= group) return;  // padding head of the last block
@@ -969,7 +988,8 @@ __global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p
       o += red[k][threadIdx.x];
       l += red_l[k];
     }
-    static_cast<bf16_t*>(p.out)[(size_t(b) * hq + g * group + hb * GB + h) * D + threadIdx.x] = f32_to_bf16(o / l);
+    static_cast<bf16_t*>(p.out)[(size_t(row_token(p.kv, b)) * hq + g * group + hb * GB + h) * D + threadIdx.x] =
+        f32_to_bf16(o / l);
   }
 }
 

@@ -50,7 +50,26 @@ kvc::LayerView layer_view(const kvc_cache* c, int32_t layer) {
   v.rolling = c->rolling;
   v.k_scale = c->dtype == KVC_I8 ? c->k_scale + size_t(layer) * layer_vecs : nullptr;
   v.v_scale = c->dtype == KVC_I8 ? c->v_scale + size_t(layer) * layer_vecs : nullptr;
+  v.cu_tokens = nullptr;  // the same T tokens in every row, unless a ragged call sets it
+  v.n_tokens = 0;
+  v.max_tokens = 0;
+  v.row_filter = kvc::kRowsAll;
   return v;
+}
+
+// A ragged call's rows: row b brings tokens [cu_tokens[b], cu_tokens[b+1]) of the packed tensors.
+void set_ragged(kvc::LayerView& v, const int32_t* cu_tokens, int32_t n_tokens, int32_t max_tokens, int filter) {
+  v.cu_tokens = cu_tokens;
+  v.n_tokens = n_tokens;
+  v.max_tokens = max_tokens;
+  v.row_filter = filter;
+}
+
+int check_ragged(const kvc_cache* c, const int32_t* cu_tokens, int32_t n_tokens, int32_t max_tokens) {
+  if (!cu_tokens || (reinterpret_cast<uintptr_t>(cu_tokens) & 3u)) return KVC_E_ARG;
+  if (n_tokens < 0 || max_tokens < 1) return KVC_E_ARG;
+  if (int64_t(c->batch) * max_tokens > 0x7fffffffLL) return KVC_E_ARG;
+  return KVC_OK;
 }
 
 bool resolve_scale(float scale, int32_t head_dim, float* out) {
@@ -105,13 +124,11 @@ size_t decode_ws_bytes(const kvc_cache* c, int32_t n_q_heads, int32_t n_workers)
 
 int launch_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_E_LAUNCH; }
 
-}  // namespace
-
-extern "C" {
-
-int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* q_out, const void* k_new,
-                    const void* v_new, int32_t T, int32_t n_q_heads, float rope_base, int32_t* dev_err,
-                    void* stream) {
+// Validation and launch shared by the uniform and the ragged append (T: tokens per
+// row, or the bound on them).
+int rope_append_impl(const kvc_cache* cache, int32_t layer, const void* q, void* q_out, const void* k_new,
+                     const void* v_new, int32_t T, int32_t n_q_heads, float rope_base, const int32_t* cu_tokens,
+                     int32_t n_tokens, int32_t* dev_err, void* stream) {
   int st = check_cache(cache);
   if (st != KVC_OK) return st;
   if (layer < 0 || layer >= cache->n_layers || T < 1) return KVC_E_ARG;
@@ -123,6 +140,7 @@ int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* 
   if (cache->rolling && T > cache->max_seq) return KVC_E_ARG;  // one call must not overwrite its own tokens
   kvc::RopeAppendParams p;
   p.kv = layer_view(cache, layer);
+  if (cu_tokens) set_ragged(p.kv, cu_tokens, n_tokens, T, kvc::kRowsAll);
   p.q = q;
   p.q_out = q_out;
   p.k_new = k_new;
@@ -135,6 +153,88 @@ int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* 
   p.dev_err = dev_err;
   if (cache->dtype == KVC_I8) return launch_status(kvc::launch_rope_append_q8(p, static_cast<hipStream_t>(stream)));
   return launch_status(kvc::launch_rope_append(p, static_cast<hipStream_t>(stream)));
+}
+
+// The split-KV decode of bfloat16 and int8 caches over the rows a layer view selects.
+int decode_bf16_impl(const kvc_cache* cache, const kvc::LayerView& lv, const void* q_rot, void* out,
+                     int32_t n_q_heads, float sc, int32_t n_workers, void* workspace, int32_t* dev_err,
+                     hipStream_t s) {
+  const DecodePlan pl = decode_plan(cache, n_q_heads, n_workers);
+  if (pl.n_wg <= 0) return KVC_E_LAUNCH;
+  // Flattened tile indices and in-row byte offsets are 32-bit.
+  const int64_t tiles = int64_t(cache->batch) * cache->n_kv_heads * pl.n_hb * ((int64_t(cache->max_seq) + 31) / 32);
+  const int64_t row_span = int64_t(cache->max_seq) * cache->n_kv_heads * cache->head_dim * 2;  // bfloat16 bound
+  if (tiles >= (int64_t(1) << 31) || row_span >= (int64_t(1) << 31)) return KVC_E_SHAPE;
+  if (int64_t(cache->batch) * cache->n_kv_heads * pl.n_hb * pl.gb > 0x7fffffffLL) return KVC_E_SHAPE;
+  kvc::DecodeParams p;
+  p.kv = lv;
+  p.q = q_rot;
+  p.out = out;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + size_t(pl.n_wg) * 2 * pl.gb * cache->head_dim;
+  p.n_q_heads = n_q_heads;
+  p.n_wg = pl.n_wg;
+  p.gb = pl.gb;
+  p.n_hb = pl.n_hb;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.dev_err = dev_err;
+  return launch_status(kvc::launch_decode_bf16(p, s));
+}
+
+// The bfloat16 prefill kernel over the rows a layer view selects (T: tokens per row, or their bound).
+int prefill_bf16_impl(const kvc_cache* cache, const kvc::LayerView& lv, const void* q_rot, void* out, int32_t T,
+                      int32_t n_q_heads, float sc, int32_t* dev_err, hipStream_t s) {
+  // The kernel's buffer descriptors span one head row with 32-bit byte offsets.
+  if (int64_t(cache->max_seq) * cache->n_kv_heads * cache->head_dim * 2 >= (int64_t(1) << 31)) return KVC_E_SHAPE;
+  kvc::PrefillParams p;
+  p.kv = lv;
+  p.q = q_rot;
+  p.out = out;
+  p.T = T;
+  p.n_q_heads = n_q_heads;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.dev_err = dev_err;
+  return launch_status(kvc::launch_prefill_mfma(p, s));
+}
+
+// Float32: one split spanning the whole cache per query row, written directly.
+int prefill_f32_impl(const kvc_cache* cache, const kvc::LayerView& lv, const void* q_rot, void* out, int32_t T,
+                     int32_t n_q_heads, float sc, int32_t* dev_err, hipStream_t s) {
+  kvc::SplitParams p;
+  p.kv = lv;
+  p.q = q_rot;
+  p.out = out;
+  p.T = T;
+  p.n_q_heads = n_q_heads;
+  p.split_keys = int32_t((int64_t(cache->max_seq) + 63) / 64 * 64);
+  p.max_splits = 1;
+  p.direct = 1;
+  p.ws_o = nullptr;
+  p.ws_ml = nullptr;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.dev_err = dev_err;
+  return launch_status(kvc::launch_split_attention(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_rope_append(const kvc_cache* cache, int32_t layer, const void* q, void* q_out, const void* k_new,
+                    const void* v_new, int32_t T, int32_t n_q_heads, float rope_base, int32_t* dev_err,
+                    void* stream) {
+  return rope_append_impl(cache, layer, q, q_out, k_new, v_new, T, n_q_heads, rope_base, nullptr, 0, dev_err,
+                          stream);
+}
+
+int kvc_rope_append_ragged(const kvc_cache* cache, int32_t layer, const void* q, void* q_out, const void* k_new,
+                           const void* v_new, const int32_t* cu_tokens, int32_t n_tokens, int32_t max_tokens,
+                           int32_t n_q_heads, float rope_base, int32_t* dev_err, void* stream) {
+  int st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if ((st = check_ragged(cache, cu_tokens, n_tokens, max_tokens)) != KVC_OK) return st;
+  return rope_append_impl(cache, layer, q, q_out, k_new, v_new, max_tokens, n_q_heads, rope_base, cu_tokens,
+                          n_tokens, dev_err, stream);
 }
 
 size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int32_t n_workers) {
@@ -157,28 +257,9 @@ int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, vo
   const size_t need = decode_ws_bytes(cache, n_q_heads, n_workers);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return KVC_E_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (cache->dtype != KVC_F32) {  // bfloat16 or int8 cache
-    const DecodePlan pl = decode_plan(cache, n_q_heads, n_workers);
-    if (pl.n_wg <= 0) return KVC_E_LAUNCH;
-    // Flattened tile indices and in-row byte offsets are 32-bit.
-    const int64_t tiles = int64_t(cache->batch) * cache->n_kv_heads * pl.n_hb * ((int64_t(cache->max_seq) + 31) / 32);
-    const int64_t row_span = int64_t(cache->max_seq) * cache->n_kv_heads * cache->head_dim * 2;  // bfloat16 bound
-    if (tiles >= (int64_t(1) << 31) || row_span >= (int64_t(1) << 31)) return KVC_E_SHAPE;
-    if (int64_t(cache->batch) * cache->n_kv_heads * pl.n_hb * pl.gb > 0x7fffffffLL) return KVC_E_SHAPE;
-    kvc::DecodeParams p;
-    p.kv = layer_view(cache, layer);
-    p.q = q_rot;
-    p.out = out;
-    p.ws_o = static_cast<float*>(workspace);
-    p.ws_ml = p.ws_o + size_t(pl.n_wg) * 2 * pl.gb * cache->head_dim;
-    p.n_q_heads = n_q_heads;
-    p.n_wg = pl.n_wg;
-    p.gb = pl.gb;
-    p.n_hb = pl.n_hb;
-    p.scale_log2 = sc * 1.4426950408889634f;
-    p.dev_err = dev_err;
-    return launch_status(kvc::launch_decode_bf16(p, s));
-  }
+  if (cache->dtype != KVC_F32)  // bfloat16 or int8 cache
+    return decode_bf16_impl(cache, layer_view(cache, layer), q_rot, out, n_q_heads, sc, n_workers, workspace,
+                            dev_err, s);
   // float32: split-KV over fixed 512-key splits.
   kvc::SplitParams p;
   p.scale_log2 = sc * 1.4426950408889634f;
@@ -212,34 +293,42 @@ int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, v
   hipStream_t s = static_cast<hipStream_t>(stream);
   kvc::LayerView lv = layer_view(cache, layer);
   lv.rolling = 0;  // prefill keeps the linear rule P + T <= max_seq, rolling window or not
-  if (cache->dtype == KVC_BF16) {
-    // The kernel's buffer descriptors span one head row with 32-bit byte offsets.
-    if (int64_t(cache->max_seq) * cache->n_kv_heads * cache->head_dim * 2 >= (int64_t(1) << 31)) return KVC_E_SHAPE;
-    kvc::PrefillParams p;
-    p.kv = lv;
-    p.q = q_rot;
-    p.out = out;
-    p.T = T;
-    p.n_q_heads = n_q_heads;
-    p.scale_log2 = sc * 1.4426950408889634f;
-    p.dev_err = dev_err;
-    return launch_status(kvc::launch_prefill_mfma(p, s));
+  if (cache->dtype == KVC_BF16) return prefill_bf16_impl(cache, lv, q_rot, out, T, n_q_heads, sc, dev_err, s);
+  return prefill_f32_impl(cache, lv, q_rot, out, T, n_q_heads, sc, dev_err, s);
+}
+
+int kvc_attn_mixed(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out, const int32_t* cu_tokens,
+                   int32_t n_tokens, int32_t max_tokens, int32_t n_q_heads, float scale, int32_t n_workers,
+                   void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream) {
+  int st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (layer < 0 || layer >= cache->n_layers) return KVC_E_ARG;
+  if ((st = check_ragged(cache, cu_tokens, n_tokens, max_tokens)) != KVC_OK) return st;
+  if (!q_rot || !out || !aligned16(q_rot) || !aligned16(out)) return KVC_E_ARG;
+  if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
+  if (n_workers < 0) return KVC_E_ARG;
+  float sc;
+  if (!resolve_scale(scale, cache->head_dim, &sc)) return KVC_E_ARG;
+  if (cache->dtype == KVC_I8) return KVC_E_DTYPE;  // its prefill rows need a bfloat16 or float32 cache
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->dtype == KVC_F32) {
+    // One launch: a direct split per query row handles decode and prefill rows alike.
+    kvc::LayerView lv = layer_view(cache, layer);
+    set_ragged(lv, cu_tokens, n_tokens, max_tokens, kvc::kRowsAll);
+    return prefill_f32_impl(cache, lv, q_rot, out, max_tokens, n_q_heads, sc, dev_err, s);
   }
-  // float32: one split spanning the whole cache per query row, written directly.
-  kvc::SplitParams p;
-  p.kv = lv;
-  p.q = q_rot;
-  p.out = out;
-  p.T = T;
-  p.n_q_heads = n_q_heads;
-  p.split_keys = int32_t((int64_t(cache->max_seq) + 63) / 64 * 64);
-  p.max_splits = 1;
-  p.direct = 1;
-  p.ws_o = nullptr;
-  p.ws_ml = nullptr;
-  p.scale_log2 = sc * 1.4426950408889634f;
-  p.dev_err = dev_err;
-  return launch_status(kvc::launch_split_attention(p, s));
+  const size_t need = decode_ws_bytes(cache, n_q_heads, n_workers);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return KVC_E_WORKSPACE;
+  if (max_tokens > 1) {  // rows with a chunk: the matrix-core prefill, linear rule as in kvc_attn_prefill
+    kvc::LayerView lv = layer_view(cache, layer);
+    lv.rolling = 0;
+    set_ragged(lv, cu_tokens, n_tokens, max_tokens, kvc::kRowsPrefill);
+    if ((st = prefill_bf16_impl(cache, lv, q_rot, out, max_tokens, n_q_heads, sc, dev_err, s)) != KVC_OK) return st;
+  }
+  // rows with one token: the split-KV decode over those rows only
+  kvc::LayerView lv = layer_view(cache, layer);
+  set_ragged(lv, cu_tokens, n_tokens, max_tokens, kvc::kRowsDecode);
+  return decode_bf16_impl(cache, lv, q_rot, out, n_q_heads, sc, n_workers, workspace, dev_err, s);
 }
 
 int kvc_decode_step(const kvc_cache* cache, int32_t layer, const void* q, const void* k_new, const void* v_new,

@@ -18,7 +18,34 @@ struct LayerView {
   float* k_scale;  // int8 caches: (batch, n_kv_heads, max_seq) scales of this layer; else null
   float* v_scale;
   int32_t rolling;  // rolling window: position p in slot p mod max_seq
+  // Ragged calls: row b brings tokens [cu_tokens[b], cu_tokens[b+1]) of the packed
+  // q / k_new / v_new / out; null for calls with the same T tokens in every row.
+  const int32_t* cu_tokens;
+  int32_t n_tokens, max_tokens;  // ragged calls: packed token rows; bound on any row's count
+  int32_t row_filter;            // kRowsAll, or one half of a mixed call (see row_selected)
 };
+
+constexpr int kRowsAll = 0;       // every row of the batch
+constexpr int kRowsDecode = 1;    // mixed call, decode launch: rows with exactly one token
+constexpr int kRowsPrefill = 2;   // mixed call, prefill launch: rows with more than one token
+
+// Row b's first packed token and token count in a call with T tokens per row
+// (ragged calls: from cu_tokens).  count = -1: a malformed range (negative,
+// decreasing, past n_tokens or longer than max_tokens) -- the row is skipped.
+struct RowTokens {
+  int first, count;
+};
+__device__ __forceinline__ RowTokens row_tokens(const LayerView& kv, int b, int T) {
+  if (!kv.cu_tokens) return RowTokens{b * T, T};
+  const int a = kv.cu_tokens[b], e = kv.cu_tokens[b + 1];
+  if (a < 0 || e < a || e > kv.n_tokens || e - a > kv.max_tokens) return RowTokens{0, -1};
+  return RowTokens{a, e - a};
+}
+// Whether a row with `count` new tokens belongs to this launch.
+__device__ __forceinline__ bool row_selected(const LayerView& kv, int count) {
+  if (count < 0) return false;
+  return kv.row_filter == kRowsAll || (kv.row_filter == kRowsDecode ? count == 1 : count > 1);
+}
 
 // Keys query t (of T new tokens of row b, P = seqlens[b]) attends, or -1 if the
 // row is out of range (skipped, KVC_DEV_CAPACITY).  Linear cache, or T > 1:

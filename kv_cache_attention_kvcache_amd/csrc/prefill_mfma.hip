@@ -91,9 +91,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
   const int b = rest / hq;
   const int g = h / group;
 
+  // This row's new tokens (ragged calls: its own count, packed from `tok0`; the
+  // grid is sized for max_tokens) and whether this launch handles it.
+  const RowTokens rt = row_tokens(p.kv, b, p.T);
+  if (!row_selected(p.kv, rt.count)) {
+    if (rt.count < 0 && qt == 0 && h == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_TOKENS);
+    return;
+  }
+  const int T = rt.count;
+  const size_t tok0 = size_t(rt.first);
+  if (qt * kBM >= T) return;  // a query tile past this row's tokens
   const int start = p.kv.seqlens[b];
-  if (start < 0 || start > p.kv.max_seq - p.T) {
-    if (qt == n_qt - 1 && h == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
+  if (start < 0 || start > p.kv.max_seq - T) {
+    if (qt == 0 && h == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
     return;
   }
   const int tid = threadIdx.x;
@@ -104,8 +114,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
 
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kWQ;                       // this wave's first query
-  const int kend_wg = start + min(q0 + kBM, p.T);        // keys the workgroup needs
-  const int kend_w = qw0 < p.T ? start + min(qw0 + kWQ, p.T) : 0;  // keys this wave needs
+  const int kend_wg = start + min(q0 + kBM, T);          // keys the workgroup needs
   const int n_tiles = (kend_wg + kBN - 1) / kBN;
 
   // The wave's queries as MFMA B operand: lane holds query qw0 + l32,
@@ -114,10 +123,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
   const int my_pos = start + my_t;
   uint4 qf[kKD];
   {
-    const bf16_t* qrow = static_cast<const bf16_t*>(p.q) + (size_t(b) * p.T + my_t) * hq * D + size_t(h) * D;
+    const bf16_t* qrow = static_cast<const bf16_t*>(p.q) + (tok0 + my_t) * hq * D + size_t(h) * D;
 #pragma unroll
     for (int kd = 0; kd < kKD; ++kd)
-      qf[kd] = my_t < p.T ? *reinterpret_cast<const uint4*>(qrow + 16 * kd + 8 * half) : make_uint4(0, 0, 0, 0);
+      qf[kd] = my_t < T ? *reinterpret_cast<const uint4*>(qrow + 16 * kd + 8 * half) : make_uint4(0, 0, 0, 0);
   }
 
   const size_t key_stride = size_t(hkv) * D;
@@ -327,9 +336,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
 
   // ---- normalise and store: o[db] register r holds head dim 32 db + 8 (r >> 2) + 4 half + (r & 3).
   const float l_tot = l + __shfl_xor(l, 32);
-  if (my_t < p.T) {
+  if (my_t < T) {
     const float inv = 1.f / l_tot;
-    bf16_t* orow = static_cast<bf16_t*>(p.out) + (size_t(b) * p.T + my_t) * hq * D + size_t(h) * D;
+    bf16_t* orow = static_cast<bf16_t*>(p.out) + (tok0 + my_t) * hq * D + size_t(h) * D;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll

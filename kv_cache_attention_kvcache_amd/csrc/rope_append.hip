@@ -48,11 +48,19 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendParams p) {
   __shared__ __align__(16) float cs[HALF];
   __shared__ __align__(16) float sn[HALF];
 
-  const int row = blockIdx.x;  // b * T + t
-  const int b = row / p.T;
-  const int t = row - b * p.T;
+  // Grid: batch x T (ragged calls: T = max_tokens).  Workgroup (b, t) takes row b's
+  // token t, which is packed row `row` of q / q_out / k_new / v_new.
+  const int b = blockIdx.x / p.T;
+  const int t = blockIdx.x - b * p.T;
+  const RowTokens rt = row_tokens(p.kv, b, p.T);
+  if (rt.count < 0) {
+    if (t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_TOKENS);
+    return;
+  }
+  if (t >= rt.count) return;
+  const int row = rt.first + t;
   const int start = p.kv.seqlens[b];
-  if (start < 0 || (!p.kv.rolling && start > p.kv.max_seq - p.T)) {
+  if (start < 0 || (!p.kv.rolling && start > p.kv.max_seq - rt.count)) {
     if (t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
     return;
   }
@@ -116,11 +124,19 @@ __global__ __launch_bounds__(256) void rope_append_q8_kernel(RopeAppendParams p)
   __shared__ __align__(16) float cs[HALF];
   __shared__ __align__(16) float sn[HALF];
 
-  const int row = blockIdx.x;  // b * T + t
-  const int b = row / p.T;
-  const int t = row - b * p.T;
+  // Grid: batch x T (ragged calls: T = max_tokens).  Workgroup (b, t) takes row b's
+  // token t, which is packed row `row` of q / q_out / k_new / v_new.
+  const int b = blockIdx.x / p.T;
+  const int t = blockIdx.x - b * p.T;
+  const RowTokens rt = row_tokens(p.kv, b, p.T);
+  if (rt.count < 0) {
+    if (t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_TOKENS);
+    return;
+  }
+  if (t >= rt.count) return;
+  const int row = rt.first + t;
   const int start = p.kv.seqlens[b];
-  if (start < 0 || (!p.kv.rolling && start > p.kv.max_seq - p.T)) {
+  if (start < 0 || (!p.kv.rolling && start > p.kv.max_seq - rt.count)) {
     if (t == 0 && threadIdx.x == 0) report(p.dev_err, KVC_DEV_CAPACITY);
     return;
   }

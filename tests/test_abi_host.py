@@ -32,9 +32,9 @@ def _declared():
 
 
 def test_header_declares_the_four_calls_and_helpers():
-    assert _declared() == sorted(["kvc_rope_append", "kvc_decode_workspace_bytes", "kvc_attn_decode",
-                                  "kvc_attn_prefill", "kvc_decode_step", "kvc_prefill_clone",
-                                  "kvc_status_string"])
+    assert _declared() == sorted(["kvc_rope_append", "kvc_rope_append_ragged", "kvc_decode_workspace_bytes",
+                                  "kvc_attn_decode", "kvc_attn_prefill", "kvc_attn_mixed", "kvc_decode_step",
+                                  "kvc_prefill_clone", "kvc_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -193,3 +193,39 @@ def test_rolling_window_validation(lib):
     bad = _desc(lib)
     bad.rolling = 2
     assert L.kvc_attn_decode(ctypes.byref(bad), 0, q, q, 16, 0.0, 0, P(0x70000), 1 << 30, None, None) == lib.KVC_E_ARG
+
+
+def test_ragged_calls_validation(lib):
+    """kvc_rope_append_ragged and kvc_attn_mixed reject bad token layouts and caches before launching."""
+    L = lib.lib
+    q, cu = P(0x40000), P(0x80000)
+    d = _desc(lib, max_seq=4096)  # batch 3, 4 KV heads, bfloat16
+
+    def app(desc=d, cu=cu, n=10, mx=8, hq=16, base=1e4):
+        return L.kvc_rope_append_ragged(ctypes.byref(desc), 0, q, q, q, q, cu, n, mx, hq, base, None, None)
+
+    assert app(cu=None) == lib.KVC_E_ARG
+    assert app(cu=P(0x80002)) == lib.KVC_E_ARG  # misaligned prefix array
+    assert app(n=-1) == lib.KVC_E_ARG
+    assert app(mx=0) == lib.KVC_E_ARG
+    assert app(hq=6) == lib.KVC_E_SHAPE
+    assert app(base=1.0) == lib.KVC_E_ARG
+    rolling = _desc(lib, max_seq=100)
+    rolling.rolling = 1
+    assert app(desc=rolling, mx=101) == lib.KVC_E_ARG  # a row longer than the window
+
+    def mix(desc=d, cu=cu, n=10, mx=8, hq=16, ws=P(0x90000), ws_bytes=1 << 30, nw=0, scale=0.0):
+        return L.kvc_attn_mixed(ctypes.byref(desc), 0, q, q, cu, n, mx, hq, scale, nw, ws, ws_bytes, None, None)
+
+    assert mix(cu=None) == lib.KVC_E_ARG
+    assert mix(mx=0) == lib.KVC_E_ARG
+    assert mix(n=-5) == lib.KVC_E_ARG
+    assert mix(nw=-1) == lib.KVC_E_ARG
+    assert mix(scale=float("nan")) == lib.KVC_E_ARG
+    assert mix(hq=5) == lib.KVC_E_SHAPE
+    assert mix(ws=None, ws_bytes=0, nw=8) == lib.KVC_E_WORKSPACE  # the decode rows need the split-KV scratch
+    assert mix(ws_bytes=8 * 2 * 4 * 130 * 4 - 4, nw=8) == lib.KVC_E_WORKSPACE  # one float short
+    i8 = _desc(lib, dtype=lib.KVC_I8)
+    i8.k_scale, i8.v_scale = 0x50000, 0x60000
+    assert mix(desc=i8) == lib.KVC_E_DTYPE
+    assert L.kvc_attn_mixed(None, 0, q, q, cu, 1, 1, 16, 0.0, 0, None, 0, None, None) == lib.KVC_E_ARG
