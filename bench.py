@@ -33,6 +33,11 @@ prefill from the front while a throttled host link loads stored chunks from
 the back) and compares it with computing only and loading only, over a range
 of simulated link speeds.
 
+`--workload mixed` times one serving step over a ragged batch of eight 72K-token
+rows: seven decode one token while the eighth prefills a 2048-token chunk
+(kvc_rope_append_ragged + kvc_attn_mixed), beside the decode-only and
+chunk-only steps.
+
 `--workload tiny` instead times the two tiny fp32 workloads' decode steps
 (one attention layer at batch 1; the six-layer tiny GPT at batch 16), which
 are bound by kernel launches: per step through kvc_rope_append +
@@ -85,7 +90,7 @@ def measured_traffic(name: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=["long_context", "long_context_int8", "tiny", "cake"],
+    ap.add_argument("--workload", choices=["long_context", "long_context_int8", "tiny", "cake", "mixed"],
                     default="long_context")
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
@@ -137,6 +142,8 @@ def main():
         return bench_int8(args)
     if args.workload == "cake":
         return bench_cake(args)
+    if args.workload == "mixed":
+        return bench_mixed(args)
     import kv_cache_attention_kvcache_amd as kvc
     import synth
 
@@ -341,6 +348,86 @@ def bench_cake(args):
         "links": rows,
         "roofline": {"bound": "io+mfma", "note": "a scheduler: the time is set by the slower of the two "
                      "sides at their meeting point, not by one kernel"}}), flush=True)
+
+
+def bench_mixed(args):
+    """One serving step over a ragged batch at the long-context shapes; one JSON line.
+
+    Eight rows of 73,728 cached tokens (64 q / 8 kv heads, head_dim 128, bf16): seven decode one
+    token each while the eighth prefills a 2048-token chunk at position 73,728 (Cake paper,
+    Section 3: a chunk of one request beside the decode tokens of others).  A step is
+    kvc_rope_append_ragged + kvc_attn_mixed over the packed 2055 tokens.  The same step with only
+    the decode rows and with only the chunk is timed beside it, so that the mixed step can be
+    compared with the sum of its parts.
+    """
+    import kv_cache_attention_kvcache_amd as kvc
+    import synth
+
+    w = synth.LONG_CONTEXT
+    ctx, hq, hkv, d = w.extra["context"], w.n_q_heads, w.n_kv_heads, w.head_dim
+    rows, chunk = 8, 2048
+    max_seq = ctx + chunk + 16
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20251)
+    cache = kvc.KVCache.empty(1, rows, max_seq, hkv, d, dtype=torch.bfloat16, device=dev)
+    cache.k.normal_(generator=gen)  # the cached history: N(0, 1) values standing for rotated keys
+    cache.v.normal_(generator=gen)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    layouts = {"mixed": [1] * (rows - 1) + [chunk], "decode_only": [1] * (rows - 1) + [0],
+               "prefill_only": [0] * (rows - 1) + [chunk]}
+    inputs = {}
+    for name, counts in layouts.items():
+        rb = kvc.RaggedBatch(counts, device=dev)
+        n = rb.n_tokens
+        q = torch.randn((n, hq, d), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((n, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((n, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+        inputs[name] = (rb, q, k, v, torch.empty_like(q), torch.empty_like(q))
+    ws = torch.empty(kvc.kvc_decode_workspace_bytes(cache, hq), dtype=torch.uint8, device=dev)
+    K = max(1, args.steps) * 5
+    res_t = {}
+    for name, (rb, q, k, v, q_rot, out) in inputs.items():
+        def step():
+            cache.seqlens.fill_(ctx)  # every step writes the same slots: constant work
+            kvc.kvc_rope_append_ragged(cache, 0, q, k, v, rb, q_out=q_rot, dev_err=err)
+            kvc.kvc_attn_mixed(cache, 0, q_rot, rb, out=out, workspace=ws, dev_err=err)
+        for _ in range(max(1, args.warmup) * 2):
+            step()
+        torch.cuda.synchronize()
+        t_step, t_attn = Timer(), Timer()
+        for _ in range(K):
+            cache.seqlens.fill_(ctx)
+            with t_step:
+                kvc.kvc_rope_append_ragged(cache, 0, q, k, v, rb, q_out=q_rot, dev_err=err)
+                with t_attn:
+                    kvc.kvc_attn_mixed(cache, 0, q_rot, rb, out=out, workspace=ws, dev_err=err)
+        torch.cuda.synchronize()
+        res_t[name] = {"step_us": round(sum(t_step.times_ms()) / K * 1e3, 1),
+                       "attention_us": round(sum(t_attn.times_ms()) / K * 1e3, 1),
+                       "tokens": rb.n_tokens}
+        log(f"{name}: {res_t[name]}", args.quiet)
+    assert err.item() == 0, f"device error bits {err.item()}"
+    m, dec, pre = res_t["mixed"], res_t["decode_only"], res_t["prefill_only"]
+    pre_flops = 4 * d * hq * (chunk * ctx + chunk * (chunk + 1) // 2)
+    dec_bytes = (rows - 1) * (ctx + 1) * hkv * d * 2 * 2
+    pre_tflops = pre_flops / (pre["attention_us"] * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": "mixed prefill+decode step: new tokens/s", "value": round(m["tokens"] / (m["step_us"] * 1e-6), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(m["step_us"] / 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "long_context_72k_mixed_step", "rows": rows, "context": ctx, "chunk": chunk,
+                   "decode_rows": rows - 1, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "parallelism": "none"},
+        "steps_us": res_t,
+        "sum_of_parts_us": round(dec["step_us"] + pre["step_us"], 1),
+        "mixed_over_sum_of_parts": round(m["step_us"] / (dec["step_us"] + pre["step_us"]), 4),
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel over the chunk row (prefill-only step's attention)",
+                     "achieved": round(pre_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": int(pre_flops), "avg_launch_us": pre["attention_us"]},
+        "decode_rows_gbps": round(dec_bytes / (dec["attention_us"] * 1e-6) / 1e9, 1),
+    }), flush=True)
 
 
 def bench_int8(args):

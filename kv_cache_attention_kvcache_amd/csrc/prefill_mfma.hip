@@ -71,16 +71,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
   const int group = hq / hkv;
   const int n_qt = (p.T + kBM - 1) / kBM;
   // XCD-aware order.  Workgroup x runs on XCD x mod 8, and each XCD starts its
-  // workgroups in the order of x / 8.  When the (row, head) pairs split evenly
-  // over the 8 XCDs, XCD i takes the consecutive pairs [i rpx, (i + 1) rpx) --
-  // the query heads of one KV head, which share its K/V stream through that
-  // XCD's L2 -- and starts all their latest (longest) query tiles first, then
-  // the next latest, and so on.  Otherwise workgroups go in plain order.
+  // workgroups in the order of x / 8.  The query heads of one KV head share its
+  // K/V stream, so they go to one XCD, whose L2 serves them all.  When the
+  // (row, KV head) groups split evenly over the 8 XCDs, group k goes to XCD
+  // k mod 8: every XCD gets a share of every row, so rows of unequal length (a
+  // ragged call's chunk beside idle rows) still spread over the whole chip.
+  // Within an XCD, all its heads' latest (longest) query tiles start first,
+  // then the next latest, and so on.  Otherwise, when at least the (row, query
+  // head) pairs split evenly, XCD i takes a consecutive run of them, in the
+  // same longest-first order; else workgroups go in plain order.
   const int x = blockIdx.x;
   int qt, rest;
-  if ((hq * p.kv.batch) % 8 == 0) {
+  if ((p.kv.batch * hkv) % 8 == 0) {
     const int rpx = hq * p.kv.batch / 8;  // (row, head) pairs per XCD
     const int j = x / 8;                  // start order within the XCD
+    qt = n_qt - 1 - j / rpx;
+    const int r = j % rpx;
+    const int kg = (r / group) * 8 + x % 8;  // (row, KV head) group b * hkv + g
+    rest = (kg / hkv) * hq + (kg % hkv) * group + r % group;
+  } else if ((hq * p.kv.batch) % 8 == 0) {
+    const int rpx = hq * p.kv.batch / 8;
+    const int j = x / 8;
     qt = n_qt - 1 - j / rpx;
     rest = (x % 8) * rpx + j % rpx;
   } else {
