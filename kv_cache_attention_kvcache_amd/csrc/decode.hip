@@ -1,5 +1,7 @@
 // Split-KV flash-decode on vector ALUs (no MFMA): the attention of one query
-// token per (row, head) against the whole cached prefix.
+// token per (row, head) against the whole cached prefix.  The same kernel,
+// with one split per query row written directly, is the float32 prefill and
+// the float32 mixed call (rows (b, t) for t below the row's token count).
 //
 // Tiny-GPT post, Gotcha 2: a decode query sees every cached key.  nanochat
 // post: attention runs against the full cache, the KV heads shared by groups

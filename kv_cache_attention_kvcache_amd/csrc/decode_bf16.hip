@@ -19,6 +19,8 @@
 // segment writes the normalised output, any other run a float32 partial
 // (unnormalised o, running max, sum).  A workgroup writes at most two partials
 // (its first run and its last), and the combine kernel folds them per segment.
+// In a ragged call (the decode half of kvc_attn_mixed) only rows with exactly
+// one new token have tiles, and a row's query and output sit at its packed row.
 //
 // One 32-key tile, per wave:
 //   * K and V are read with coalesced 16-byte buffer loads, 16 lanes per

@@ -25,6 +25,10 @@
 //   * Workgroups are ordered so that the query heads sharing a KV head run
 //     on the same XCD (its L2 serves their common K/V stream), longest
 //     (latest) query tiles first.
+//   * In a ragged call (the prefill half of kvc_attn_mixed) each row has its
+//     own token count and first packed row; the grid covers the largest count
+//     and workgroups past a row's tokens, or of rows with fewer than two
+//     tokens, return at once.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 #include "kvc.h"

@@ -9,7 +9,8 @@
 // and writes the same amount.  A workgroup takes one (row, token): it
 // evaluates cos/sin of the token's head_dim/2 angles once into LDS, then
 // rotates every q head and k head with 4-pair vectors and copies v with
-// 16-byte vectors.
+// 16-byte vectors.  The grid is batch x T; in a ragged call T is the bound on
+// any row's tokens, and a workgroup past its row's count returns at once.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 #include "kvc.h"
