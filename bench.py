@@ -505,7 +505,7 @@ def bench_int8(args):
                      "unit": "GB/s", "frac": round(per_launch / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "traffic": None, "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_ms * 1e3, 2),
                      "note": "codes + float32 scales per launch; the products run on bf16 matrix cores, "
-                             "and one workgroup per CU with two tiles in flight streams about 55% of peak"}}),
+                             "one workgroup per CU and one tile in flight per wave"}}),
           flush=True)
 
 
