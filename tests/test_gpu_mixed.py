@@ -147,3 +147,39 @@ def test_malformed_token_ranges_are_skipped(kvc, dtype):
         qh = rope.rotate_round(numerics.round_to(q[:cnt], dtype), pos, dtype)
         ref = oatt.attend(qh, np.concatenate([hist_k[0], k_new]), np.concatenate([hist_v[0], v_new]), pos)
         gates.check(host64(out[:cnt]), ref, dtype, f"row 0 beside malformed rows {cu}")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 16, 4, 128), ("f32", 4, 4, 64)])
+def test_mixed_batch_on_a_rolling_window(kvc, dtype, hq, hkv, d):
+    """On a rolling cache the decode rows attend the window of the last max_seq positions and
+    the prefill rows keep the linear rule (P + T <= max_seq): checked against the oracle's
+    sliding-window attention over the raw history (Tiny-GPT post, "The Cache, in Code")."""
+    window = 128
+    starts, counts = [0, 130, 300, 50], [5, 1, 1, 2]  # rows 1 and 2 have wrapped; 0 and 3 prefill
+    g = _rng(42, hq, d)
+    b_sz, n_hist = len(starts), max(s + c for s, c in zip(starts, counts))
+    q = g.standard_normal((b_sz, n_hist, hq, d)).astype(np.float32)
+    k = g.standard_normal((b_sz, n_hist, hkv, d)).astype(np.float32)
+    v = g.standard_normal((b_sz, n_hist, hkv, d)).astype(np.float32)
+    cache = make_cache(kvc, 1, b_sz, window, hkv, d, dtype)
+    cache = kvc.KVCache(cache.k, cache.v, cache.seqlens, rolling=True)
+    for b, p in enumerate(starts):  # the window's history: position i in slot i mod window
+        pos = np.arange(max(0, p - window), p)
+        if len(pos):
+            slots = torch.from_numpy(pos % window).cuda()
+            cache.k[0, b, slots] = dev(rope.rotate_round(numerics.round_to(k[b, pos], dtype), pos, dtype), dtype)
+            cache.v[0, b, slots] = dev(numerics.round_to(v[b, pos], dtype), dtype)
+    cache.seqlens.copy_(torch.tensor(starts, dtype=torch.int32))
+    rb = kvc.RaggedBatch(counts)
+    qp = np.concatenate([q[b, s:s + c] for b, (s, c) in enumerate(zip(starts, counts))])
+    kp = np.concatenate([k[b, s:s + c] for b, (s, c) in enumerate(zip(starts, counts))])
+    vp = np.concatenate([v[b, s:s + c] for b, (s, c) in enumerate(zip(starts, counts))])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q_rot = kvc.kvc_rope_append_ragged(cache, 0, dev(qp, dtype), dev(kp, dtype), dev(vp, dtype), rb, dev_err=err)
+    out = host64(kvc.kvc_attn_mixed(cache, 0, q_rot, rb, dev_err=err))
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    for b, (s, c) in enumerate(zip(starts, counts)):
+        first = rb.first(b)
+        ref = oatt.window_outputs(q[b], k[b], v[b], list(range(s, s + c)), window, dtype)
+        gates.check(out[first:first + c], ref, dtype, f"rolling mixed row {b} ({c} tokens at {s})")
