@@ -491,6 +491,13 @@ def bench_int8(args):
     total = K * (dec_bytes[1] + dec_bytes[rows]) / ((ms[1] + ms[rows]) * 1e-3) / 1e9
     per_launch = dec_bytes[rows] / n_dec
     avg_ms = ms[rows] / (K * n_dec)
+    if args.copy_probe_mib > 0:  # a known-size copy that calibrates the profiler's byte counters
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps({
         "metric": "KV-cache decode attn HBM GB/s on an int8 cache (codes + scales)", "value": round(total, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 2),
@@ -503,7 +510,8 @@ def bench_int8(args):
         "roofline": {"bound": "hbm", "kernel": "decode_q8_mfma_kernel + decode_bf16_combine_kernel, batch 8",
                      "achieved": round(per_launch / (avg_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(per_launch / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "traffic": measured_traffic("decode_q8_b8_72k"), "bytes_per_launch": int(per_launch),
+                     "avg_launch_us": round(avg_ms * 1e3, 2),
                      "note": "codes + float32 scales per launch; the products run on bf16 matrix cores, "
                              "one workgroup per CU and one tile in flight per wave"}}),
           flush=True)
