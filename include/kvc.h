@@ -215,7 +215,9 @@ int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, v
  * and the tensors are (n_tokens, heads, head_dim).  A row whose range is
  * malformed (cu_tokens[b] < 0, a decreasing pair, an end past n_tokens, or
  * T_b > max_tokens) is skipped and KVC_DEV_TOKENS is set; nothing outside the
- * packed rows is ever read or written.  A row with T_b = 0 is left alone.
+ * packed rows is ever read or written.  A row with T_b = 0 is left alone, and
+ * a call with n_tokens = 0 returns KVC_OK without launching anything (its
+ * tensor pointers may then be null).
  * Otherwise each row follows the rules of the uniform calls with T = T_b.
  */
 

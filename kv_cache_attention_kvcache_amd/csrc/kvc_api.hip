@@ -233,6 +233,8 @@ int kvc_rope_append_ragged(const kvc_cache* cache, int32_t layer, const void* q,
   int st = check_cache(cache);
   if (st != KVC_OK) return st;
   if ((st = check_ragged(cache, cu_tokens, n_tokens, max_tokens)) != KVC_OK) return st;
+  if (layer < 0 || layer >= cache->n_layers) return KVC_E_ARG;
+  if (n_tokens == 0) return KVC_OK;  // no row brings a token: nothing to read or write
   return rope_append_impl(cache, layer, q, q_out, k_new, v_new, max_tokens, n_q_heads, rope_base, cu_tokens,
                           n_tokens, dev_err, stream);
 }
@@ -304,6 +306,7 @@ int kvc_attn_mixed(const kvc_cache* cache, int32_t layer, const void* q_rot, voi
   if (st != KVC_OK) return st;
   if (layer < 0 || layer >= cache->n_layers) return KVC_E_ARG;
   if ((st = check_ragged(cache, cu_tokens, n_tokens, max_tokens)) != KVC_OK) return st;
+  if (n_tokens == 0) return KVC_OK;  // no row brings a token: nothing to attend
   if (!q_rot || !out || !aligned16(q_rot) || !aligned16(out)) return KVC_E_ARG;
   if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
   if (n_workers < 0) return KVC_E_ARG;

@@ -229,3 +229,17 @@ def test_ragged_calls_validation(lib):
     i8.k_scale, i8.v_scale = 0x50000, 0x60000
     assert mix(desc=i8) == lib.KVC_E_DTYPE
     assert L.kvc_attn_mixed(None, 0, q, q, cu, 1, 1, 16, 0.0, 0, None, 0, None, None) == lib.KVC_E_ARG
+
+
+def test_empty_ragged_calls_are_no_ops(lib):
+    """n_tokens = 0 (every row idle): validated, then nothing is launched, so null tensors are fine."""
+    L = lib.lib
+    d = _desc(lib, max_seq=4096)
+    cu = P(0x80000)
+    assert L.kvc_rope_append_ragged(ctypes.byref(d), 0, None, None, None, None, cu, 0, 1, 16, 1e4, None,
+                                    None) == lib.KVC_OK
+    assert L.kvc_attn_mixed(ctypes.byref(d), 0, None, None, cu, 0, 1, 16, 0.0, 0, None, 0, None, None) == lib.KVC_OK
+    # the layout is still validated first
+    assert L.kvc_rope_append_ragged(ctypes.byref(d), 0, None, None, None, None, None, 0, 1, 16, 1e4, None,
+                                    None) == lib.KVC_E_ARG
+    assert L.kvc_attn_mixed(ctypes.byref(d), 5, None, None, cu, 0, 1, 16, 0.0, 0, None, 0, None, None) == lib.KVC_E_ARG
