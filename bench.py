@@ -294,7 +294,7 @@ def main():
         torch.cuda.synchronize()
         res["copy_probe_bytes"] = n
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, kv_bytes_tok, q_)
+        res["cpu_baseline"] = cpu_baseline(w, kv_bytes_tok, q_, step_decode_bytes=dec_bytes[1] + dec_bytes[rows])
     print(json.dumps(res), flush=True)
 
 
@@ -656,7 +656,7 @@ class _Null:
         return False
 
 
-def cpu_baseline(w, kv_bytes_tok, quiet):
+def cpu_baseline(w, kv_bytes_tok, quiet, step_decode_bytes=None):
     """The oracle, as it is, on the host: no-cache decode of one token at the full
     73,728-token context (every key re-rotated from its raw value, all 64 heads),
     repeated until about 10 s have passed.  Rate in K/V bytes per second, like `value`."""
@@ -688,9 +688,16 @@ def cpu_baseline(w, kv_bytes_tok, quiet):
     dt = time.time() - t0
     bytes_per = (ctx + 1) * kv_bytes_tok
     log(f"cpu baseline: {n} oracle decode calls in {dt:.1f}s", quiet)
-    return {"value": round(n * bytes_per / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} no-cache decode calls of one token at context {ctx + 1} (64 q / 8 kv heads, "
-                      f"all keys re-rotated from raw), {dt:.1f} s"}
+    rate = n * bytes_per / dt
+    res = {"value": round(rate / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{n} no-cache decode calls of one token at context {ctx + 1} (64 q / 8 kv heads, "
+                     f"all keys re-rotated from raw), {dt:.1f} s"}
+    if step_decode_bytes:
+        # the no-cache oracle's cost is linear in the keys it re-reads, so one step's decode
+        # calls (batch 1 and batch 8) take their K/V bytes over the sampled rate
+        res["extrapolated_step_decode_s"] = round(step_decode_bytes / rate, 1)
+        res["extrapolation"] = "linear in K/V bytes from the sample to one timed step's decode calls"
+    return res
 
 
 if __name__ == "__main__":
