@@ -20,7 +20,8 @@
 //     transposed in registers with byte permutes while staging), P^T comes
 //     straight from the score registers rounded to bfloat16.
 //   * Only tiles that reach past a wave's first query position are masked;
-//     fully hidden tiles are never loaded.  The next tile's K/V is fetched
+//     fully hidden tiles are never loaded.  P*V of the previous tile runs
+//     beside the softmax of the current one.  The next tile's K/V is fetched
 //     into registers while the current one is computed.
 //   * Workgroups are ordered so that the query heads sharing a KV head run
 //     on the same XCD (its L2 serves their common K/V stream), longest
@@ -210,18 +211,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
   const int arow = perm_row(l32);
 
   // S^T of one tile: 2 blocks of 32 keys, the first k-step from a zero accumulator.
+  // All 16 K fragments are read first; the two blocks' chains alternate.
   auto qk = [&](int buf, f32x16_t* s) {
+    uint4 kf[2 * kKD];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t* arow_p = k_lds[buf] + (32 * kb + arow) * kKStride + 16 * half;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kd = 0; kd < kKD; ++kd) {
-        const uint4 a = *reinterpret_cast<const uint4*>(arow_p + 32 * kd);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+      for (int kd = 0; kd < kKD; ++kd)
+        kf[kb * kKD + kd] =
+            *reinterpret_cast<const uint4*>(k_lds[buf] + (32 * kb + arow) * kKStride + 16 * half + 32 * kd);
+#pragma unroll
+    for (int kd = 0; kd < kKD; ++kd)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[kb * kKD + kd]),
                                                         __builtin_bit_cast(bf16x8_t, qf[kd]),
                                                         kd == 0 ? f32x16_t{} : s[kb], 0, 0, 0);
-      }
-    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKD, 0);  // every K fragment read first
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kKD, 0);  // then the score MFMAs
   };
   // Keys past a query's position get score -inf.  Only tiles that reach past
   // the wave's first query need it; a tile wholly past every query of the wave
@@ -241,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
   };
   // Probabilities of one tile's (masked) scores against the running maximum
   // m, as the bfloat16 B operands of P*V, and the sum of the rounded values
-  // in lt.  Branch-free, so that it interleaves with the next tile's score
+  // in lt.  Branch-free, so that it interleaves with the previous tile's P*V
   // MFMAs.  No per-tile maximum is taken first: the caller checks lt instead.
   auto probs = [&](const f32x16_t* s, uint4* pf, float& lt) {
     lt = 0.f;
@@ -278,43 +285,33 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
     probs(s, pf, lt);
     return alpha;
   };
-  // O^T += V^T P^T for one tile.
-  auto pv = [&](int buf, const uint4* pf) {
+  // The V^T fragments of one tile (A operands of the 4 k-steps x kDB output blocks).
+  auto read_v = [&](int buf, uint4* vf) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const uint4 a = *reinterpret_cast<const uint4*>(v_lds[buf] + (32 * db + l32) * kVStride + 32 * ks + 16 * half);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                        __builtin_bit_cast(bf16x8_t, pf[ks]), o[db], 0, 0, 0);
-      }
-    }
+      for (int db = 0; db < kDB; ++db)
+        vf[ks * kDB + db] =
+            *reinterpret_cast<const uint4*>(v_lds[buf] + (32 * db + l32) * kVStride + 32 * ks + 16 * half);
   };
-
-  // Software pipeline over the workgroup's tiles.  Entering iteration t (after
-  // a barrier): K(t+1) sits in k_lds[(t+1)&1], V(t) in v_lds[t&1], the masked
-  // S(t) in registers, and the staging registers hold K(t+2) and V(t+1).  The
-  // iteration issues the score MFMAs of tile t+1 alongside the softmax of tile
-  // t (one branch-free block), stores K(t+2) and V(t+1) into the buffers the
-  // last barrier freed, starts the loads of K(t+3) and V(t+2), and accumulates
-  // P(t) V(t): one barrier per tile.  Loads past the last tile read zeros (the
-  // range check), so every step runs unconditionally.
-  auto step = [&](int t, f32x16_t* s_cur, f32x16_t* s_next) {
-    uint4 pf[4];  // B operands of the 4 k-steps of 16 keys
+  // O^T += V^T P^T for one tile.
+  auto pv = [&](const uint4* vf, const uint4* pf) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[ks * kDB + db]),
+                                                        __builtin_bit_cast(bf16x8_t, pf[ks]), o[db], 0, 0, 0);
+  };
+  // Softmax of one tile's masked scores into pf, with the lazy rescale of o and l.
+  auto soft = [&](f32x16_t* s, uint4* pf) {
     float lt;
-    qk((t + 1) & 1, s_next);
-    probs(s_cur, pf, lt);
-    // Keep the softmax in the block of the score MFMAs it overlaps with: an
-    // empty asm that consumes its results stops the compiler from sinking the
-    // exponentials past the branches below, next to their P*V use.
-    asm volatile("" ::"v"(pf[0].x), "v"(pf[0].y), "v"(pf[0].z), "v"(pf[0].w), "v"(pf[1].x), "v"(pf[1].y),
-                 "v"(pf[1].z), "v"(pf[1].w), "v"(pf[2].x), "v"(pf[2].y), "v"(pf[2].z), "v"(pf[2].w), "v"(pf[3].x),
-                 "v"(pf[3].y), "v"(pf[3].z), "v"(pf[3].w), "v"(lt));
+    probs(s, pf, lt);
     if (__ballot(!(lt <= kLazyBound)) != 0) {
       // A real (wave-uniform) branch: without the asm the compiler if-converts
       // this block and multiplies o by alpha = 1 on every tile.
       asm volatile("");
-      const float alpha = raise_max(s_cur, pf, lt);
+      const float alpha = raise_max(s, pf, lt);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < kDB; ++db)
@@ -322,12 +319,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
     l += lt;
-    store_k(t & 1);
-    store_v((t + 1) & 1);
-    load_k(t + 3);
-    load_v(t + 2);
-    mask(t + 1, s_next);
-    pv(t & 1, pf);
+  };
+
+  // Software pipeline over the workgroup's tiles.  Entering step j (after a
+  // barrier): K(j) sits in k_lds[j&1], V(j-1) in v_lds[(j-1)&1], P(j-1) in
+  // registers, and the staging registers hold K(j+1) and V(j).  The step issues
+  // the score MFMAs of tile j, stores K(j+1) and V(j) into the buffers the last
+  // barrier freed, starts the loads of K(j+2) and V(j+1), reads the V^T
+  // fragments of tile j-1, masks S(j), then accumulates P(j-1) V(j-1) beside
+  // the softmax of tile j: one barrier per tile.  Loads past the last tile read
+  // zeros (the range check), so every step runs unconditionally.
+  auto step = [&](int j, const uint4* pf_prev, uint4* pf_cur) {
+    f32x16_t s[2];
+    uint4 vf[4 * kDB];
+    qk(j & 1, s);
+    store_k((j + 1) & 1);
+    store_v(j & 1);
+    load_k(j + 2);
+    load_v(j + 1);
+    read_v((j - 1) & 1, vf);
+    mask(j, s);
+    pv(vf, pf_prev);
+    soft(s, pf_cur);
     __syncthreads();
   };
   load_k(0);
@@ -339,15 +352,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
   load_v(1);
   load_k(2);
   __syncthreads();
-  f32x16_t sa[2], sb[2];
-  qk(0, sa);
-  mask(0, sa);
-  int t = 0;
-  for (; t + 1 < n_tiles; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
+  uint4 pa[4], pb[4];  // P(j) of even and odd tiles
+  {
+    f32x16_t s[2];
+    qk(0, s);
+    mask(0, s);
+    soft(s, pa);
   }
-  if (t < n_tiles) step(t, sa, sb);
+  int j = 1;
+  for (; j + 1 < n_tiles; j += 2) {
+    step(j, pa, pb);
+    step(j + 1, pb, pa);
+  }
+  if (j < n_tiles) step(j, pa, pb);
+  {
+    uint4 vf[4 * kDB];
+    read_v((n_tiles - 1) & 1, vf);
+    pv(vf, ((n_tiles - 1) & 1) ? pb : pa);
+  }
 
   // ---- normalise and store: o[db] register r holds head dim 32 db + 8 (r >> 2) + 4 half + (r & 3).
   const float l_tot = l + __shfl_xor(l, 32);
