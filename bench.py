@@ -20,8 +20,11 @@ oracle timed on a bounded sample of the same work.
 After the timed steps the default run also measures two ceilings of the chip
 (kv_cache_attention_kvcache_amd.ceilings): the best streaming-read rate in
 decode's access shape (256-byte rows at a 2 KiB stride) and the best bfloat16
-matrix-core rate, and states each roofline against them as well as against
-the published peaks.
+matrix-core rate, with constant operands and with random operands that change
+every product (the matrix cores then draw more power and the chip holds a
+lower clock), and states each roofline against them as well as against the
+published peaks: the prefill against the random-operand rate, the data it
+computes on being random.
 
 `--workload long_context_int8` runs the same decode steps on an int8 cache
 (codes plus one float32 scale per cached vector): the 72K context is written
@@ -281,7 +284,8 @@ def main():
         torch.cuda.synchronize()
         c = ceilings.measure(dev)
         res["measured_ceilings"] = c
-        for key, probe in (("roofline", "hbm_read_rows_gbps"), ("roofline_prefill", "mfma_bf16_tflops")):
+        res["roofline_prefill"]["measured_ceiling_constant_operands"] = c["mfma_bf16_tflops"]["value"]
+        for key, probe in (("roofline", "hbm_read_rows_gbps"), ("roofline_prefill", "mfma_bf16_random_tflops")):
             res[key]["measured_ceiling"] = c[probe]["value"]
             res[key]["frac_of_measured"] = round(res[key]["achieved"] / c[probe]["value"], 4)
         log(f"measured ceilings: {c}", q_)

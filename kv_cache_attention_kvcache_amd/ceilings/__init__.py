@@ -14,7 +14,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc_ceilings.so")
-EXPORTS = ("kvc_ceiling_stream_read", "kvc_ceiling_mfma_bf16")
+EXPORTS = ("kvc_ceiling_stream_read", "kvc_ceiling_mfma_bf16", "kvc_ceiling_lds_read")
 MFMA_FLOPS = 32768  # one 32x32x16 product: 2 * 32 * 32 * 16 flops
 
 _lib = None
@@ -29,9 +29,11 @@ def _load():
         lib.kvc_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         lib.kvc_ceiling_stream_read.restype = ctypes.c_int
-        lib.kvc_ceiling_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                              ctypes.c_void_p]
+        lib.kvc_ceiling_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p]
         lib.kvc_ceiling_mfma_bf16.restype = ctypes.c_int
+        lib.kvc_ceiling_lds_read.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        lib.kvc_ceiling_lds_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -54,13 +56,21 @@ def stream_read(buf: torch.Tensor, row_bytes: int, stride_bytes: int, nontempora
     return rows * row_bytes
 
 
-def mfma_bf16(iters: int, chains: int, workgroups: int, sink: torch.Tensor) -> float:
-    """Launch the matrix-core loop; returns its flops."""
-    rc = _load().kvc_ceiling_mfma_bf16(iters, chains, workgroups, ctypes.c_void_p(sink.data_ptr()),
-                                       _stream_ptr())
+def mfma_bf16(iters: int, chains: int, workgroups: int, sink: torch.Tensor, random_operands: bool = False) -> float:
+    """Launch the matrix-core loop (8 x chains products per wave per iteration); returns its flops."""
+    rc = _load().kvc_ceiling_mfma_bf16(iters, chains, int(random_operands), workgroups,
+                                       ctypes.c_void_p(sink.data_ptr()), _stream_ptr())
     if rc != 0:
         raise RuntimeError(f"kvc_ceiling_mfma_bf16 failed ({rc})")
-    return float(workgroups) * 4 * iters * chains * MFMA_FLOPS
+    return float(workgroups) * 4 * iters * 8 * chains * MFMA_FLOPS
+
+
+def lds_read(iters: int, workgroups: int, sink: torch.Tensor) -> int:
+    """Launch the LDS read loop (8 waves per workgroup); returns the bytes it reads from LDS."""
+    rc = _load().kvc_ceiling_lds_read(iters, workgroups, ctypes.c_void_p(sink.data_ptr()), _stream_ptr())
+    if rc != 0:
+        raise RuntimeError(f"kvc_ceiling_lds_read failed ({rc})")
+    return workgroups * 8 * iters * 16384
 
 
 def _timed(fn, reps: int) -> float:
@@ -85,7 +95,15 @@ def measure(device=None, buffer_gib: int = 4, reps: int = 5) -> dict:
       dims), the bytes of the rows only.
     * mfma_bf16_tflops: two or four independent 32x32x16 bfloat16 chains
       per wave, one or two 4-wave workgroups per CU (one or two waves per
-      SIMD).
+      SIMD), with constant operands.
+    * mfma_bf16_random_tflops: the same loop on random operands that change
+      from one product to the next, as attention's do.  The matrix cores
+      draw more power on such data and the chip lowers its clock, so this is
+      the rate a bfloat16 contraction over random data can reach.
+    * lds_read_tbps: the prefill kernel's LDS operand reads (16-byte reads
+      of a padded 16 KB tile, 8 waves per workgroup) at one or two
+      workgroups per CU, in TB/s over the whole chip; `bytes_per_clk_per_cu`
+      states it per CU at the 2.4 GHz peak clock.
     """
     dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -105,14 +123,24 @@ def measure(device=None, buffer_gib: int = 4, reps: int = 5) -> dict:
                         best, shapes[name] = rate, {"nontemporal": nt, "workgroups_per_cu": wpc}
             shapes[name]["value"] = round(best, 1)
         del buf
+        for name, rnd in (("mfma_bf16_tflops", False), ("mfma_bf16_random_tflops", True)):
+            best = 0.0
+            for chains in (2, 4):
+                for wpc in (1, 2):
+                    iters = 10000 // chains
+                    fl = float(cus * wpc) * 4 * iters * 8 * chains * MFMA_FLOPS
+                    t = _timed(lambda: mfma_bf16(iters, chains, cus * wpc, sink, rnd), reps)
+                    rate = fl / t / 1e12
+                    if rate > best:
+                        best, shapes[name] = rate, {"chains": chains, "workgroups_per_cu": wpc,
+                                                    "random_operands": rnd}
+            shapes[name]["value"] = round(best, 1)
         best = 0.0
-        for chains in (2, 4):
-            for wpc in (1, 2):
-                iters = 80000 // chains
-                fl = float(cus * wpc) * 4 * iters * chains * MFMA_FLOPS
-                t = _timed(lambda: mfma_bf16(iters, chains, cus * wpc, sink), reps)
-                rate = fl / t / 1e12
-                if rate > best:
-                    best, shapes["mfma_bf16_tflops"] = rate, {"chains": chains, "workgroups_per_cu": wpc}
-        shapes["mfma_bf16_tflops"]["value"] = round(best, 1)
+        for wpc in (1, 2):
+            nbytes = cus * wpc * 8 * 4000 * 16384
+            t = _timed(lambda: lds_read(4000, cus * wpc, sink), reps)
+            if nbytes / t / 1e12 > best:
+                best, shapes["lds_read_tbps"] = nbytes / t / 1e12, {"workgroups_per_cu": wpc}
+        shapes["lds_read_tbps"]["value"] = round(best, 1)
+        shapes["lds_read_tbps"]["bytes_per_clk_per_cu"] = round(best * 1e12 / cus / 2.4e9, 1)
     return shapes

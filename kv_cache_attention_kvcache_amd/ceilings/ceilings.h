@@ -29,10 +29,21 @@ int kvc_ceiling_stream_read(const void* buf, int64_t rows, int32_t row_bytes, in
                             int32_t nontemporal, int32_t workgroups, uint32_t* sink, hipStream_t stream);
 
 // Every wave of `workgroups` workgroups of 256 threads runs `iters` rounds of
-// `chains` (2 or 4) independent v_mfma_f32_32x32x16_bf16 accumulations
-// (32768 flops each); *sink is written only for an impossible result.
-// Flops per call = workgroups * 4 waves * iters * chains * 32768.
-int kvc_ceiling_mfma_bf16(int32_t iters, int32_t chains, int32_t workgroups, float* sink, hipStream_t stream);
+// 8 x `chains` (chains 2 or 4) v_mfma_f32_32x32x16_bf16 products (32768 flops
+// each), cycling through 8 A and 8 B operand registers; *sink is written only
+// for an impossible result.  random_operands == 0: every operand register holds
+// one small constant pattern.  random_operands != 0: A uniform in [-2, 2) and B
+// uniform in [0, 1), different per register and lane, as attention's scores and
+// weights are; the matrix cores then draw more power and the clock they hold
+// can be lower.  Flops per call = workgroups * 4 waves * iters * 8 * chains * 32768.
+int kvc_ceiling_mfma_bf16(int32_t iters, int32_t chains, int32_t random_operands, int32_t workgroups, float* sink,
+                          hipStream_t stream);
+
+// Every wave of `workgroups` workgroups of 512 threads (8 waves) reads, `iters`
+// times, a 16 KB tile from LDS in the prefill kernel's MFMA-operand pattern: 16
+// ds_read_b128 per lane, rows of 256 data bytes padded to 272.  *sink is written
+// only for an impossible XOR.  Bytes read per call = workgroups * 8 * iters * 16384.
+int kvc_ceiling_lds_read(int32_t iters, int32_t workgroups, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

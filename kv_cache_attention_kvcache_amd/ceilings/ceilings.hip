@@ -43,25 +43,83 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint8_t* __
   if (acc == kNeverXor) sink[0] = acc;
 }
 
-template <int CH>
+// 32-bit integer hash (multiply-xorshift) for the random operands.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+// Each wave cycles its products through 8 A and 8 B operand registers.  Constant
+// operands: every register holds the same small pattern, so the matrix cores'
+// inputs hardly change between products.  Random operands: A uniform in
+// [-2, 2) and B uniform in [0, 1) (the range of softmax weights), different in
+// every register and lane, so consecutive products see fresh data as in
+// attention.
+template <int CH, bool RANDOM>
 __global__ __launch_bounds__(kThreads) void mfma_bf16_kernel(int32_t iters, float* sink) {
-  bf16x8 a, b;
+  bf16x8 a[8], b[8];
+  const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = static_cast<__bf16>(float(threadIdx.x & 7) * 0.125f);
-    b[i] = static_cast<__bf16>(float(i) * -0.25f);
-  }
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (RANDOM) {
+        const float ua = float(mix32(t * 131u + j * 8 + i) >> 8) * (1.f / 16777216.f);
+        const float ub = float(mix32(t * 977u + j * 8 + i + 0x5555u) >> 8) * (1.f / 16777216.f);
+        a[j][i] = static_cast<__bf16>(ua * 4.f - 2.f);
+        b[j][i] = static_cast<__bf16>(ub);
+      } else {
+        a[j][i] = static_cast<__bf16>(float(threadIdx.x & 7) * 0.125f);
+        b[j][i] = static_cast<__bf16>(float(i) * -0.25f);
+      }
+    }
   f32x16 c[CH];
 #pragma unroll
   for (int k = 0; k < CH; ++k) c[k] = f32x16{};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int k = 0; k < CH; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < CH; ++k)
+        c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(k + u) & 7], b[(3 * k + u) & 7], c[k], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < CH; ++k) s += c[k][0] + c[k][15];
   if (s == 1.2345e30f) sink[0] = s;
+}
+
+// LDS reads in the prefill kernel's pattern: each of a workgroup's 8 waves reads
+// a 64-row tile of 272-byte rows (256 bytes of data + 16 of padding) as 16
+// MFMA A fragments (lane (l32, half) reads 16 bytes at row perm(l32) + 32 kb,
+// byte 16 half + 32 kd), every iteration, and folds them into an XOR.
+constexpr int kLdsThreads = 512;
+constexpr int kLdsRow = 272;
+
+__global__ __launch_bounds__(kLdsThreads) void lds_read_kernel(int32_t iters, uint32_t* sink) {
+  __shared__ __align__(16) uint8_t tile[64 * kLdsRow];
+  const int tid = threadIdx.x, half = (tid & 63) >> 5, l32 = tid & 31;
+  for (int i = tid; i < 64 * kLdsRow / 16; i += kLdsThreads)
+    reinterpret_cast<u32x4*>(tile)[i] = u32x4{uint32_t(i), uint32_t(i) * 3u, uint32_t(i) * 5u, uint32_t(i) * 7u};
+  __syncthreads();
+  const int row = ((l32 >> 4) << 4) | (((l32 >> 2) & 1) << 3) | (((l32 >> 3) & 1) << 2) | (l32 & 3);
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" ::: "memory");  // the tile is read again every iteration
+    u32x4 f[16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int kd = 0; kd < 8; ++kd)
+        f[kb * 8 + kd] = *reinterpret_cast<const u32x4*>(tile + (32 * kb + row) * kLdsRow + 16 * half + 32 * kd);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc += f[i].x ^ f[i].y ^ f[i].z ^ f[i].w;
+  }
+  if (acc == kNeverXor) sink[0] = acc;
 }
 
 }  // namespace
@@ -82,12 +140,22 @@ extern "C" int kvc_ceiling_stream_read(const void* buf, int64_t rows, int32_t ro
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
-extern "C" int kvc_ceiling_mfma_bf16(int32_t iters, int32_t chains, int32_t workgroups, float* sink,
-                                     hipStream_t stream) {
+extern "C" int kvc_ceiling_mfma_bf16(int32_t iters, int32_t chains, int32_t random_operands, int32_t workgroups,
+                                     float* sink, hipStream_t stream) {
   if (!sink || iters < 1 || workgroups < 1 || (chains != 2 && chains != 4)) return -1;
-  if (chains == 2)
-    hipLaunchKernelGGL(mfma_bf16_kernel<2>, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
-  else
-    hipLaunchKernelGGL(mfma_bf16_kernel<4>, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+  const dim3 grid(workgroups), block(kThreads);
+  if (random_operands) {
+    if (chains == 2) hipLaunchKernelGGL((mfma_bf16_kernel<2, true>), grid, block, 0, stream, iters, sink);
+    else hipLaunchKernelGGL((mfma_bf16_kernel<4, true>), grid, block, 0, stream, iters, sink);
+  } else {
+    if (chains == 2) hipLaunchKernelGGL((mfma_bf16_kernel<2, false>), grid, block, 0, stream, iters, sink);
+    else hipLaunchKernelGGL((mfma_bf16_kernel<4, false>), grid, block, 0, stream, iters, sink);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" int kvc_ceiling_lds_read(int32_t iters, int32_t workgroups, uint32_t* sink, hipStream_t stream) {
+  if (!sink || iters < 1 || workgroups < 1) return -1;
+  hipLaunchKernelGGL(lds_read_kernel, dim3(workgroups), dim3(kLdsThreads), 0, stream, iters, sink);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }

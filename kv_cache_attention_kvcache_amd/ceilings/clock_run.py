@@ -2,7 +2,8 @@
 
     python -m kv_cache_attention_kvcache_amd.ceilings.clock_run
 
-runs, on cuda:0: the matrix-core ceiling loop three times; the causal prefill
+runs, on cuda:0: the matrix-core ceiling loop three times with constant
+operands and three times with random ones; the causal prefill
 of the last 4096-token chunk of a 73,728-token context six times (64 q / 8 kv
 heads, head_dim 128, bf16); and twenty batch-8 decodes at that context.
 Under `rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE ...` each dispatch then
@@ -29,8 +30,9 @@ def main() -> None:
     hq, hkv, d, t_chunk, start = 64, 8, 128, 4096, 69632
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    for _ in range(3):
-        ceilings.mfma_bf16(20000, 4, cus * 2, sink)
+    for rnd in (False, True):
+        for _ in range(3):
+            ceilings.mfma_bf16(2500, 4, cus * 2, sink, random_operands=rnd)
     cache = kvc.KVCache.empty(1, 1, start + t_chunk, hkv, d, dtype=bf, device=dev)
     cache.k.normal_(generator=gen)
     cache.v.normal_(generator=gen)

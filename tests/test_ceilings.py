@@ -68,9 +68,14 @@ def test_null_and_misaligned_pointers_rejected(ceil):
     assert lib.kvc_ceiling_stream_read(ctypes.c_void_p(0x10008), 4, 256, 256, 0, 1,
                                        ctypes.c_void_p(0x20000), None) == -1
     assert lib.kvc_ceiling_stream_read(ctypes.c_void_p(0x10000), 4, 256, 256, 0, 1, None, None) == -1
-    assert lib.kvc_ceiling_mfma_bf16(10, 2, 1, None, None) == -1
-    assert lib.kvc_ceiling_mfma_bf16(0, 2, 1, ctypes.c_void_p(0x20000), None) == -1
-    assert lib.kvc_ceiling_mfma_bf16(10, 3, 1, ctypes.c_void_p(0x20000), None) == -1
+    for rnd in (0, 1):
+        assert lib.kvc_ceiling_mfma_bf16(10, 2, rnd, 1, None, None) == -1
+        assert lib.kvc_ceiling_mfma_bf16(0, 2, rnd, 1, ctypes.c_void_p(0x20000), None) == -1
+        assert lib.kvc_ceiling_mfma_bf16(10, 3, rnd, 1, ctypes.c_void_p(0x20000), None) == -1
+        assert lib.kvc_ceiling_mfma_bf16(10, 2, rnd, 0, ctypes.c_void_p(0x20000), None) == -1
+    assert lib.kvc_ceiling_lds_read(10, 1, None, None) == -1
+    assert lib.kvc_ceiling_lds_read(0, 1, ctypes.c_void_p(0x20000), None) == -1
+    assert lib.kvc_ceiling_lds_read(10, 0, ctypes.c_void_p(0x20000), None) == -1
 
 
 @pytest.mark.gpu
@@ -82,6 +87,10 @@ def test_measured_ceilings_are_plausible(ceil):
     assert 3000 < c["hbm_read_gbps"]["value"] < 8000
     assert 3000 < c["hbm_read_rows_gbps"]["value"] < 8000
     assert 1500 < c["mfma_bf16_tflops"]["value"] < 2500
+    # random operands cost power, never speed: at most the constant-operand rate (plus noise)
+    assert 1000 < c["mfma_bf16_random_tflops"]["value"] < c["mfma_bf16_tflops"]["value"] * 1.02
+    # 64 banks x 4 bytes per clock per CU at 2.4 GHz over 256 CUs is 157 TB/s
+    assert 30 < c["lds_read_tbps"]["value"] < 160
 
 
 @pytest.mark.gpu
