@@ -41,6 +41,11 @@ rows: seven decode one token while the eighth prefills a 2048-token chunk
 (kvc_rope_append_ragged + kvc_attn_mixed), beside the decode-only and
 chunk-only steps.
 
+`--workload ragged_b64` times ragged batched decode: 64 rows with cached
+lengths uniform in [1, 32768] (64 q / 8 kv heads, head_dim 128, bf16), one new
+token per row; a step is 80 logical layers of RoPE+append and split-KV decode
+over 4 physical layer slices of 8.66 GB each, then seqlens += 1.
+
 `--workload tiny` instead times the two tiny fp32 workloads' decode steps
 (one attention layer at batch 1; the six-layer tiny GPT at batch 16), which
 are bound by kernel launches: per step through kvc_rope_append +
@@ -93,7 +98,7 @@ def measured_traffic(name: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=["long_context", "long_context_int8", "tiny", "cake", "mixed"],
+    ap.add_argument("--workload", choices=["long_context", "long_context_int8", "tiny", "cake", "mixed", "ragged_b64"],
                     default="long_context")
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
@@ -147,6 +152,8 @@ def main():
         return bench_cake(args)
     if args.workload == "mixed":
         return bench_mixed(args)
+    if args.workload == "ragged_b64":
+        return bench_ragged(args)
     import kv_cache_attention_kvcache_amd as kvc
     import synth
 
@@ -432,6 +439,118 @@ def bench_mixed(args):
                      "flops_per_launch": int(pre_flops), "avg_launch_us": pre["attention_us"]},
         "decode_rows_gbps": round(dec_bytes / (dec["attention_us"] * 1e-6) / 1e9, 1),
     }), flush=True)
+
+
+def bench_ragged(args):
+    """Ragged batched decode over streamed layers; one JSON line.
+
+    Batch 64 (64 q / 8 kv heads, head_dim 128, bf16), cached lengths P_b uniform in
+    [1, 32768], one new token per row with RoPE at its own offset (nanochat post: the
+    new K/V go in place at each row's cache_seqlens).  A step is 80 logical layers of
+    kvc_rope_append + kvc_attn_decode over 4 physical layer slices of 8.66 GB (logical
+    layer l uses slice l mod 4), then the caller's seqlens += 1.  Every slice is far
+    larger than the 256 MB last-level cache, so each decode call streams its K/V from
+    HBM.  The cached rows are windows of one seeded N(0, 1) pool, taken as
+    already-rotated keys.
+    """
+    import dataclasses
+
+    import kv_cache_attention_kvcache_amd as kvc
+    import synth
+
+    w = synth.RAGGED_DECODE
+    n_phys = 4
+    b_sz, hq, hkv, d = w.extra["batch"], w.n_q_heads, w.n_kv_heads, w.head_dim
+    n_logical = w.extra["logical_layers"]
+    if args.steps + args.warmup > w.max_seq - w.extra["len_max"]:
+        raise SystemExit(f"at most {w.max_seq - w.extra['len_max']} steps fit the cache's margin")
+    bf = torch.bfloat16
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lengths = synth.ragged_lengths(w)
+    offs = synth.ragged_offsets(dataclasses.replace(w, extra={**w.extra, "physical_layers": n_phys}))
+    cache = kvc.KVCache.empty(n_phys, b_sz, w.max_seq, hkv, d, dtype=bf, device=dev)
+    pool = torch.from_numpy(synth.ragged_pool(w)).to(dev).to(bf)
+    for layer in range(n_phys):
+        for b in range(b_sz):
+            n_b = int(lengths[b])
+            for which, t in ((0, cache.k), (1, cache.v)):
+                o = int(offs[layer, b, which])
+                t[layer, b, :n_b] = pool[o:o + n_b * hkv * d].view(n_b, hkv, d)
+    del pool
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(bf).to(dev)
+    new = [tuple(to_dev(a) for a in synth.ragged_new_qkv(w, ell)) for ell in range(n_logical)]
+    q_rot = torch.empty((b_sz, 1, hq, d), dtype=bf, device=dev)
+    out = torch.empty_like(q_rot)
+    ws = torch.empty(kvc.kvc_decode_workspace_bytes(cache, hq), dtype=torch.uint8, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv_bytes_tok = 2 * hkv * d * 2  # K and V, bf16
+    t_dec = Timer()
+
+    def step(timed):
+        for ell in range(n_logical):
+            q, k, v = new[ell]
+            kvc.kvc_rope_append(cache, ell % n_phys, q, k, v, q_out=q_rot, dev_err=err)
+            with t_dec if timed else _Null():
+                kvc.kvc_attn_decode(cache, ell % n_phys, q_rot, out=out, workspace=ws, dev_err=err)
+        cache.seqlens += 1
+
+    cache.seqlens.copy_(torch.from_numpy(lengths))
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(False)
+        torch.cuda.synchronize()
+        log(f"warmup step {i} done", args.quiet)
+    base = int(lengths.astype(np.int64).sum()) + b_sz * args.warmup  # cached tokens entering the first timed step
+    torch.cuda.synchronize()
+    t0 = time.time()
+    for i in range(args.steps):
+        step(True)
+        log(f"timed step {i} enqueued", args.quiet)
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    assert err.item() == 0, f"device error bits {err.item()}"
+    # step s: every decode call sees P_b + s + 1 keys per row (the new token included)
+    step_bytes = [n_logical * (base + b_sz * s + b_sz) * kv_bytes_tok for s in range(args.steps)]
+    ms_dec = sum(t_dec.times_ms())
+    n_calls = args.steps * n_logical
+    gbps = sum(step_bytes) / (ms_dec * 1e-3) / 1e9
+    per_launch = sum(step_bytes) / n_calls
+    ms_step = wall * 1e3 / args.steps
+    res = {
+        "metric": "KV-cache decode attn HBM GB/s (% of peak)", "value": round(gbps, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": b_sz, "len_range": [1, w.extra["len_max"]],
+                   "mean_cached_len": round(base / b_sz, 1), "q_heads": hq, "kv_heads": hkv, "head_dim": d,
+                   "logical_layers": n_logical, "physical_layer_slices": n_phys,
+                   "slice_gb": round(cache.k[0].numel() * 2 * 2 / 1e9, 2), "parallelism": "none"},
+        "decode_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(b_sz / (ms_step * 1e-3), 1),
+        "decode_ms_per_step": round(ms_dec / args.steps, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode (decode_bf16_kernel + decode_bf16_combine_kernel), batch 64",
+                     "achieved": round(per_launch / (ms_dec / n_calls * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(per_launch / (ms_dec / n_calls * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("decode_bf16_ragged_b64"), "bytes_per_launch": int(per_launch),
+                     "avg_launch_us": round(ms_dec / n_calls * 1e3, 2)},
+    }
+    if not args.no_ceilings:
+        from kv_cache_attention_kvcache_amd import ceilings
+        del cache
+        torch.cuda.empty_cache()
+        c = ceilings.measure(dev)
+        res["roofline"]["measured_ceiling"] = c["hbm_read_rows_gbps"]["value"]
+        res["roofline"]["frac_of_measured"] = round(res["roofline"]["achieved"] / c["hbm_read_rows_gbps"]["value"], 4)
+        res["measured_ceilings"] = {k: c[k] for k in ("hbm_read_gbps", "hbm_read_rows_gbps")}
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = n
+    print(json.dumps(res), flush=True)
 
 
 def bench_int8(args):
