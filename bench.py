@@ -305,7 +305,8 @@ def main():
         torch.cuda.synchronize()
         res["copy_probe_bytes"] = n
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, kv_bytes_tok, q_, step_decode_bytes=dec_bytes[1] + dec_bytes[rows])
+        res["cpu_baseline"] = cpu_baseline(w, kv_bytes_tok, q_, step_decode_bytes=dec_bytes[1] + dec_bytes[rows],
+                                           prefill_flops=pre_flops)
     print(json.dumps(res), flush=True)
 
 
@@ -779,10 +780,14 @@ class _Null:
         return False
 
 
-def cpu_baseline(w, kv_bytes_tok, quiet, step_decode_bytes=None):
+def cpu_baseline(w, kv_bytes_tok, quiet, step_decode_bytes=None, prefill_flops=None):
     """The oracle, as it is, on the host: no-cache decode of one token at the full
     73,728-token context (every key re-rotated from its raw value, all 64 heads),
-    repeated until about 10 s have passed.  Rate in K/V bytes per second, like `value`."""
+    repeated until about 10 s have passed.  Rate in K/V bytes per second, like `value`.
+
+    With `prefill_flops`, also one no-cache call for 8 query positions spread over
+    the last prefill chunk (causal, all 64 heads), timed and stated in GFLOP/s of
+    attention, with the time the full chunked prefill would take at that rate."""
     import synth
     from oracle import attention as oatt
 
@@ -820,6 +825,22 @@ def cpu_baseline(w, kv_bytes_tok, quiet, step_decode_bytes=None):
         # calls (batch 1 and batch 8) take their K/V bytes over the sampled rate
         res["extrapolated_step_decode_s"] = round(step_decode_bytes / rate, 1)
         res["extrapolation"] = "linear in K/V bytes from the sample to one timed step's decode calls"
+    if prefill_flops:
+        chunk = w.extra["chunk"]
+        start = ctx - chunk  # the last chunk's first position
+        q_all[start:ctx] = synth.chunk_qkv(w, ctx // chunk - 1, chunk)[0]
+        pos = [start + 511 + 512 * i for i in range(8)]
+        fl = 4 * w.head_dim * w.n_q_heads * sum(p + 1 for p in pos)
+        t1 = time.time()
+        oatt.nocache_outputs(q_all, k_all, v_all, pos, "bf16")
+        dt1 = time.time() - t1
+        log(f"cpu baseline: prefill sample of {len(pos)} positions in {dt1:.1f}s", quiet)
+        res["prefill_sample"] = {
+            "gflops": round(fl / dt1 / 1e9, 3), "seconds": round(dt1, 1),
+            "sample": f"one no-cache call for {len(pos)} query positions of the last chunk ({pos[0]}..{pos[-1]}, "
+                      f"every 512th), all keys up to each re-rotated from raw, {fl / 1e9:.1f} GFLOP of attention",
+            "extrapolated_prefill_s": round(prefill_flops / (fl / dt1), 0),
+            "extrapolation": "linear in attention flops from the sample to the full 18-chunk prefill"}
     return res
 
 
