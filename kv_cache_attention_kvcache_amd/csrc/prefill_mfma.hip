@@ -359,6 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
     mask(0, s);
     soft(s, pa);
   }
+  __syncthreads();  // every wave has read K(0) before step 1 stores K(2) over it
   int j = 1;
   for (; j + 1 < n_tiles; j += 2) {
     step(j, pa, pb);
