@@ -11,7 +11,9 @@ One step = one pass of the whole hot path over the long-context workload
 All inputs are seeded, synthetic and resident in HBM before timing starts.
 
 Reported: decode attention K/V bytes per second (the JSON `value`), prefill
-attention TFLOP/s, tokens/s, a roofline record for the decode kernel pair
+attention TFLOP/s, the RoPE+append and clone bandwidths (algorithmic bytes:
+q read and written, k/v read, K/V slots written; clone source read once and
+written to every row), tokens/s, a roofline record for the decode kernel pair
 (HIP events around every decode call, on the stream they run on) and the CPU
 oracle timed on a bounded sample of the same work.
 
@@ -198,7 +200,7 @@ def main():
     out_d = {b: torch.empty((b, 1, hq, d), dtype=bf, device=dev) for b in (1, rows)}
     err = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    t_pre, t_clone, t_dec = Timer(), Timer(), {1: Timer(), rows: Timer()}
+    t_pre, t_app, t_clone, t_dec = Timer(), Timer(), Timer(), {1: Timer(), rows: Timer()}
     phase = {k: Timer() for k in ("prefill", "clone", "decode1", "decode8")}
 
     def step(timed: bool):
@@ -206,7 +208,8 @@ def main():
         cache8.seqlens.zero_()
         with phase["prefill"] if timed else _Null():
             for c in range(n_chunks):
-                kvc.kvc_rope_append(cache1, 0, pq[c], pk[c], pv[c], q_out=qrot_p, dev_err=err)
+                with t_app if timed else _Null():
+                    kvc.kvc_rope_append(cache1, 0, pq[c], pk[c], pv[c], q_out=qrot_p, dev_err=err)
                 with t_pre if timed else _Null():
                     kvc.kvc_attn_prefill(cache1, 0, qrot_p, out=out_p, dev_err=err)
                 cache1.seqlens += chunk
@@ -238,6 +241,8 @@ def main():
     kv_bytes_tok = 2 * hkv * d * 2  # K and V, bf16
     dec_bytes = {1: sum((ctx + s + 1) * kv_bytes_tok for s in range(n_dec)),
                  rows: rows * sum((ctx + s + 1) * kv_bytes_tok for s in range(n_dec))}
+    # RoPE + append of one prefill chunk: q read and q_out written, k/v read, the K and V slots written
+    app_bytes = chunk * d * 2 * (2 * hq + 4 * hkv)
     pairs = sum(chunk * (c * chunk) + chunk * (chunk + 1) // 2 for c in range(n_chunks))
     pre_flops = 4 * d * hq * pairs
     K = args.steps
@@ -251,6 +256,8 @@ def main():
     avg_launch_ms = ms_dec[rows] / (K * n_dec)
     achieved = per_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
     ph = {k: sum(v.times_ms()) / K for k, v in phase.items()}
+    clone_gbps = (ctx * kv_bytes_tok * (1 + rows)) / (sum(t_clone.times_ms()) / K * 1e-3) / 1e9
+    app_gbps = K * n_chunks * app_bytes / (sum(t_app.times_ms()) * 1e-3) / 1e9
     tokens = ctx + n_dec * (1 + rows)
     ms_step = wall * 1e3 / K
     res = {
@@ -273,7 +280,11 @@ def main():
         "prefill_tflops": round(pre_tflops, 1),
         "prefill_mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
         "prefill_ms": round(ms_pre / K, 2),
-        "clone_gbps": round((ctx * kv_bytes_tok * (1 + rows)) / (sum(t_clone.times_ms()) / K * 1e-3) / 1e9, 1),
+        "clone_gbps": round(clone_gbps, 1),
+        "clone_hbm_frac": round(clone_gbps / HBM_PEAK_GBPS, 4),
+        "append_gbps": round(app_gbps, 1),
+        "append_hbm_frac": round(app_gbps / HBM_PEAK_GBPS, 4),
+        "append_us_per_chunk": round(sum(t_app.times_ms()) / (K * n_chunks) * 1e3, 1),
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "phase_ms": {k: round(v, 3) for k, v in ph.items()},
         "roofline": {"bound": "hbm", "kernel": "decode (decode_bf16_kernel + decode_bf16_combine_kernel), batch 8",
