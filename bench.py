@@ -303,7 +303,7 @@ def main():
         c = ceilings.measure(dev)
         res["measured_ceilings"] = c
         res["roofline_prefill"]["measured_ceiling_constant_operands"] = c["mfma_bf16_tflops"]["value"]
-        for key, probe in (("roofline", "hbm_read_rows_gbps"), ("roofline_prefill", "mfma_bf16_random_tflops")):
+        for key, probe in (("roofline", "hbm_read_decode_gbps"), ("roofline_prefill", "mfma_bf16_random_tflops")):
             res[key]["measured_ceiling"] = c[probe]["value"]
             res[key]["frac_of_measured"] = round(res[key]["achieved"] / c[probe]["value"], 4)
         log(f"measured ceilings: {c}", q_)

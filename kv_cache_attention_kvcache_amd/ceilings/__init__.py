@@ -14,7 +14,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc_ceilings.so")
-EXPORTS = ("kvc_ceiling_stream_read", "kvc_ceiling_mfma_bf16", "kvc_ceiling_lds_read")
+EXPORTS = ("kvc_ceiling_stream_read", "kvc_ceiling_mfma_bf16", "kvc_ceiling_lds_read", "kvc_ceiling_decode_read")
 MFMA_FLOPS = 32768  # one 32x32x16 product: 2 * 32 * 32 * 16 flops
 
 _lib = None
@@ -34,6 +34,9 @@ def _load():
         lib.kvc_ceiling_mfma_bf16.restype = ctypes.c_int
         lib.kvc_ceiling_lds_read.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         lib.kvc_ceiling_lds_read.restype = ctypes.c_int
+        lib.kvc_ceiling_decode_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        lib.kvc_ceiling_decode_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -73,6 +76,21 @@ def lds_read(iters: int, workgroups: int, sink: torch.Tensor) -> int:
     return workgroups * 8 * iters * 16384
 
 
+def decode_read(k: torch.Tensor, v: torch.Tensor, rows: int, n_keys: int, heads: int, parts: int,
+                sink: torch.Tensor) -> int:
+    """Launch the read in the decode kernel's assignment over K and V of (rows, n_keys, heads, 256 bytes);
+    returns the bytes it reads."""
+    need = rows * n_keys * heads * 256
+    for t in (k, v):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.numel() < need:
+            raise ValueError(f"k and v must be contiguous uint8 device tensors of at least {need} bytes")
+    rc = _load().kvc_ceiling_decode_read(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), rows, n_keys,
+                                         heads, parts, ctypes.c_void_p(sink.data_ptr()), _stream_ptr())
+    if rc != 0:
+        raise RuntimeError(f"kvc_ceiling_decode_read failed ({rc})")
+    return 2 * need
+
+
 def _timed(fn, reps: int) -> float:
     """Seconds per call: one untimed call, then `reps` calls between HIP events on the current stream."""
     fn()
@@ -85,7 +103,7 @@ def _timed(fn, reps: int) -> float:
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
-def measure(device=None, buffer_gib: int = 4, reps: int = 5) -> dict:
+def measure(device=None, buffer_gib: int = 4, reps: int = 5, decode_shape=(8, 73729, 8)) -> dict:
     """The best rate of each probe over its launch shapes.
 
     * hbm_read_gbps: contiguous 16-byte loads over `buffer_gib` GiB (far past
@@ -93,6 +111,10 @@ def measure(device=None, buffer_gib: int = 4, reps: int = 5) -> dict:
     * hbm_read_rows_gbps: decode's access shape, 256-byte rows at a 2 KiB
       stride (one KV head's row of a bfloat16 cache with 8 KV heads of 128
       dims), the bytes of the rows only.
+    * hbm_read_decode_gbps: the decode kernel's whole read with no arithmetic:
+      K and V of `decode_shape` = (rows, keys, KV heads) with 256-byte head
+      rows (the batch-8 call at 73,729 keys by default), every (row, head)
+      segment cut into 4, 8 or 16 contiguous key ranges, one per workgroup.
     * mfma_bf16_tflops: two or four independent 32x32x16 bfloat16 chains
       per wave, one or two 4-wave workgroups per CU (one or two waves per
       SIMD), with constant operands.
@@ -123,6 +145,20 @@ def measure(device=None, buffer_gib: int = 4, reps: int = 5) -> dict:
                         best, shapes[name] = rate, {"nontemporal": nt, "workgroups_per_cu": wpc}
             shapes[name]["value"] = round(best, 1)
         del buf
+        rows, n_keys, heads = decode_shape
+        kbuf = torch.empty(rows * n_keys * heads * 256, dtype=torch.uint8, device=dev)
+        vbuf = torch.empty_like(kbuf)
+        kbuf.fill_(1)
+        vbuf.fill_(2)
+        best = 0.0
+        for parts in (4, 8, 16):
+            nbytes = 2 * kbuf.numel()
+            t = _timed(lambda: decode_read(kbuf, vbuf, rows, n_keys, heads, parts, sink), reps)
+            if nbytes / t / 1e9 > best:
+                best, shapes["hbm_read_decode_gbps"] = nbytes / t / 1e9, {
+                    "workgroups": rows * heads * parts, "shape": [rows, n_keys, heads, 256]}
+        shapes["hbm_read_decode_gbps"]["value"] = round(best, 1)
+        del kbuf, vbuf
         for name, rnd in (("mfma_bf16_tflops", False), ("mfma_bf16_random_tflops", True)):
             best = 0.0
             for chains in (2, 4):

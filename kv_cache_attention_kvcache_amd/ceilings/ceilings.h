@@ -28,6 +28,16 @@ extern "C" {
 int kvc_ceiling_stream_read(const void* buf, int64_t rows, int32_t row_bytes, int64_t stride_bytes,
                             int32_t nontemporal, int32_t workgroups, uint32_t* sink, hipStream_t stream);
 
+// Reads K and V laid out (rows, n_keys, heads, 256 bytes), each a contiguous,
+// 16-byte aligned device buffer of rows * n_keys * heads * 256 bytes owned by the
+// caller, in the decode kernel's assignment: rows * heads * parts workgroups of
+// 256 threads, workgroup w streaming keys [p n_keys / parts, (p + 1) n_keys / parts)
+// of segment (row, head) = divmod(w / parts, heads), p = w % parts, with
+// non-temporal 16-byte loads and no arithmetic but an XOR written to *sink only
+// for an impossible value.  Bytes read per call = 2 * rows * n_keys * heads * 256.
+int kvc_ceiling_decode_read(const void* k, const void* v, int32_t rows, int32_t n_keys, int32_t heads,
+                            int32_t parts, uint32_t* sink, hipStream_t stream);
+
 // Every wave of `workgroups` workgroups of 256 threads runs `iters` rounds of
 // 8 x `chains` (chains 2 or 4) v_mfma_f32_32x32x16_bf16 products (32768 flops
 // each), cycling through 8 A and 8 B operand registers; *sink is written only

@@ -43,6 +43,48 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint8_t* __
   if (acc == kNeverXor) sink[0] = acc;
 }
 
+// Decode's own read assignment: K and V are (rows, keys, heads, 256 bytes).  The
+// (row, head) segments are cut into `parts` contiguous key ranges, one per
+// workgroup (workgroup w: segment w / parts, part w % parts), as the decode
+// kernel deals its tiles.  The four waves take 32-key tiles of the range in turn;
+// a lane reads 16 bytes of four key rows per tile step, from K and from V, all
+// sixteen loads issued before any is consumed.
+__global__ __launch_bounds__(kThreads) void decode_read_kernel(const uint8_t* __restrict__ k,
+                                                              const uint8_t* __restrict__ v, int32_t n_keys,
+                                                              int32_t heads, int32_t parts, uint32_t* sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x / 64;
+  const int seg = blockIdx.x / parts, part = blockIdx.x % parts;
+  const int row = seg / heads, head = seg % heads;
+  const int k0 = int(int64_t(part) * n_keys / parts), k1 = int(int64_t(part + 1) * n_keys / parts);
+  const int64_t key_stride = int64_t(heads) * 256;
+  const int64_t base = (int64_t(row) * n_keys * heads + head) * 256 + (lane & 15) * 16;
+  uint32_t acc = 0;
+  for (int t = k0 + wave * 32; t < k1; t += 4 * 32) {
+    if (t + 32 <= k1) {
+      u32x4 a[kLoadsInFlight], b[kLoadsInFlight];
+#pragma unroll
+      for (int i = 0; i < kLoadsInFlight; ++i) {
+        const int64_t off = base + int64_t(t + 4 * i + lane / 16) * key_stride;
+        a[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
+        b[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
+      }
+#pragma unroll
+      for (int i = 0; i < kLoadsInFlight; ++i) acc ^= a[i].x ^ a[i].y ^ a[i].z ^ a[i].w ^ b[i].x ^ b[i].y ^ b[i].z ^ b[i].w;
+    } else {
+      for (int i = 0; i < kLoadsInFlight; ++i) {
+        const int key = t + 4 * i + lane / 16;
+        if (key < k1) {
+          const int64_t off = base + int64_t(key) * key_stride;
+          const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
+          const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
+          acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+        }
+      }
+    }
+  }
+  if (acc == kNeverXor) sink[0] = acc;
+}
+
 // 32-bit integer hash (multiply-xorshift) for the random operands.
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
@@ -157,5 +199,17 @@ extern "C" int kvc_ceiling_mfma_bf16(int32_t iters, int32_t chains, int32_t rand
 extern "C" int kvc_ceiling_lds_read(int32_t iters, int32_t workgroups, uint32_t* sink, hipStream_t stream) {
   if (!sink || iters < 1 || workgroups < 1) return -1;
   hipLaunchKernelGGL(lds_read_kernel, dim3(workgroups), dim3(kLdsThreads), 0, stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" int kvc_ceiling_decode_read(const void* k, const void* v, int32_t rows, int32_t n_keys, int32_t heads,
+                                       int32_t parts, uint32_t* sink, hipStream_t stream) {
+  if (!k || !v || !sink || rows < 1 || n_keys < 1 || heads < 1 || parts < 1 ||
+      (reinterpret_cast<uintptr_t>(k) & 15) != 0 || (reinterpret_cast<uintptr_t>(v) & 15) != 0)
+    return -1;
+  const int64_t n_wg = int64_t(rows) * heads * parts;
+  if (n_wg > 0x7fffffffLL || int64_t(n_keys) * parts > 0x7fffffffLL) return -1;
+  hipLaunchKernelGGL(decode_read_kernel, dim3(unsigned(n_wg)), dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), n_keys, heads, parts, sink);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }

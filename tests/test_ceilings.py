@@ -76,6 +76,12 @@ def test_null_and_misaligned_pointers_rejected(ceil):
     assert lib.kvc_ceiling_lds_read(10, 1, None, None) == -1
     assert lib.kvc_ceiling_lds_read(0, 1, ctypes.c_void_p(0x20000), None) == -1
     assert lib.kvc_ceiling_lds_read(10, 0, ctypes.c_void_p(0x20000), None) == -1
+    k, v, sink = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x20000)
+    assert lib.kvc_ceiling_decode_read(None, v, 8, 64, 8, 4, sink, None) == -1
+    assert lib.kvc_ceiling_decode_read(k, ctypes.c_void_p(0x40004), 8, 64, 8, 4, sink, None) == -1
+    assert lib.kvc_ceiling_decode_read(k, v, 8, 64, 8, 4, None, None) == -1
+    for rows, keys, heads, parts in ((0, 64, 8, 4), (8, 0, 8, 4), (8, 64, 0, 4), (8, 64, 8, 0)):
+        assert lib.kvc_ceiling_decode_read(k, v, rows, keys, heads, parts, sink, None) == -1
 
 
 @pytest.mark.gpu
@@ -86,6 +92,7 @@ def test_measured_ceilings_are_plausible(ceil):
     c = ceil.measure(buffer_gib=2, reps=3)
     assert 3000 < c["hbm_read_gbps"]["value"] < 8000
     assert 3000 < c["hbm_read_rows_gbps"]["value"] < 8000
+    assert 3000 < c["hbm_read_decode_gbps"]["value"] < 8000
     assert 1500 < c["mfma_bf16_tflops"]["value"] < 2500
     # random operands cost power, never speed: at most the constant-operand rate (plus noise)
     assert 1000 < c["mfma_bf16_random_tflops"]["value"] < c["mfma_bf16_tflops"]["value"] * 1.02
