@@ -25,9 +25,9 @@
  *
  * Rolling window (rolling = 1).  Tiny-GPT post, "The Cache, in Code" and "Does
  * the Cache Change the Output?": the cache keeps the last max_seq positions,
- * each rotated at its absolute position; attention scores depend only on the
- * distance between query and key, so the window can slide without
- * re-rotating.  seqlens[b] then counts every token row b has seen, and
+ * each rotated at its absolute position; under RoPE a score is a function of
+ * how far apart the two positions are, not of where they sit, so the window
+ * can slide without rotating any cached key again.  seqlens[b] then counts every token row b has seen, and
  * absolute position p lives in slot p mod max_seq.  kvc_rope_append writes
  * token t at slot (P + t) mod max_seq (T <= max_seq, else KVC_E_ARG), rotated
  * at P + t; a one-token decode (kvc_attn_decode, kvc_decode_step) attends the

@@ -100,6 +100,20 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _scratch(nbytes: int, device, stream):
+    """A temporary device buffer for one call on `stream`.  torch's caching allocator ties a block
+    to the stream it was allocated on, so a buffer used on another stream is recorded there: its
+    memory is not handed to new work until that stream's kernels are done with it."""
+    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _record(t, stream)
+    return t
+
+
+def _record(t, stream):
+    if stream is not None and t is not None:
+        t.record_stream(stream)
+
+
 def scale_shape(cache_shape):
     """Shape of an int8 cache's k_scale / v_scale for a (n_layers, batch, max_seq, n_kv_heads, head_dim)
     cache: (n_layers, batch, n_kv_heads, max_seq), head-major."""
@@ -199,6 +213,7 @@ def kvc_rope_append(cache: KVCache, layer: int, q, k_new, v_new, q_out=None, rop
     _like(v_new, cache, (cache.batch, t, cache.n_kv_heads, cache.head_dim), "v_new")
     if q_out is None:
         q_out = torch.empty_like(q)
+        _record(q_out, stream)
     _like(q_out, cache, q.shape, "q_out")
     st = lib.kvc_rope_append(cache.desc(), int(layer), _ptr(q), _ptr(q_out), _ptr(k_new), _ptr(v_new), int(t),
                              int(hq), float(rope_base), _ptr(dev_err), _stream(stream, cache.k.device))
@@ -219,10 +234,11 @@ def kvc_attn_decode(cache: KVCache, layer: int, q_rot, out=None, scale: float = 
     _like(q_rot, cache, (cache.batch, 1, hq, cache.head_dim), "q_rot")
     if out is None:
         out = torch.empty_like(q_rot)
+        _record(out, stream)
     _like(out, cache, q_rot.shape, "out")
     need = kvc_decode_workspace_bytes(cache, hq, n_workers)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=cache.k.device)
+        workspace = _scratch(need, cache.k.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kvc_attn_decode(cache.desc(), int(layer), _ptr(q_rot), _ptr(out), int(hq), float(scale),
                              int(n_workers), _ptr(workspace), ws_bytes, _ptr(dev_err),
@@ -237,6 +253,7 @@ def kvc_attn_prefill(cache: KVCache, layer: int, q_rot, out=None, scale: float =
     _like(q_rot, cache, (cache.batch, t, hq, cache.head_dim), "q_rot")
     if out is None:
         out = torch.empty_like(q_rot)
+        _record(out, stream)
     _like(out, cache, q_rot.shape, "out")
     st = lib.kvc_attn_prefill(cache.desc(), int(layer), _ptr(q_rot), _ptr(out), int(t), int(hq), float(scale),
                               _ptr(dev_err), _stream(stream, cache.k.device))
@@ -253,6 +270,7 @@ def kvc_decode_step(cache: KVCache, layer: int, q, k_new, v_new, out=None, scale
     _like(v_new, cache, (cache.batch, 1, cache.n_kv_heads, cache.head_dim), "v_new")
     if out is None:
         out = torch.empty_like(q)
+        _record(out, stream)
     _like(out, cache, q.shape, "out")
     st = lib.kvc_decode_step(cache.desc(), int(layer), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), int(hq),
                              float(scale), float(rope_base), _ptr(dev_err), _stream(stream, cache.k.device))
@@ -293,6 +311,7 @@ def kvc_rope_append_ragged(cache: KVCache, layer: int, q, k_new, v_new, rb: Ragg
     _like(v_new, cache, (rb.n_tokens, cache.n_kv_heads, cache.head_dim), "v_new")
     if q_out is None:
         q_out = torch.empty_like(q)
+        _record(q_out, stream)
     _like(q_out, cache, q.shape, "q_out")
     if rb.cu_tokens.numel() != cache.batch + 1 or rb.cu_tokens.device != cache.k.device:
         raise ValueError("the ragged batch must have batch + 1 prefix entries on the cache's device")
@@ -311,12 +330,13 @@ def kvc_attn_mixed(cache: KVCache, layer: int, q_rot, rb: RaggedBatch, out=None,
     _like(q_rot, cache, (rb.n_tokens, hq, cache.head_dim), "q_rot")
     if out is None:
         out = torch.empty_like(q_rot)
+        _record(out, stream)
     _like(out, cache, q_rot.shape, "out")
     if rb.cu_tokens.numel() != cache.batch + 1 or rb.cu_tokens.device != cache.k.device:
         raise ValueError("the ragged batch must have batch + 1 prefix entries on the cache's device")
     need = kvc_decode_workspace_bytes(cache, hq, n_workers)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=cache.k.device)
+        workspace = _scratch(need, cache.k.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kvc_attn_mixed(cache.desc(), int(layer), _ptr(q_rot), _ptr(out), _ptr(rb.cu_tokens),
                             int(rb.n_tokens), int(rb.max_tokens), int(hq), float(scale), int(n_workers),
