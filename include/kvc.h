@@ -3,9 +3,10 @@
  *
  * A C ABI over four operations and two helpers.  Every pointer named
  * "device" must point to memory on the current HIP device; the library never
- * allocates, never frees and keeps no pointer after a call returns.  Its only
- * state is a per-device cache of a read-only device property (the CU count),
- * so calls on different streams are independent.
+ * allocates, never frees and keeps no caller pointer after a call returns.
+ * Its state is per device: a cached read-only device property (the CU count)
+ * and one static scratch array that only kvc_attn_decode_noalloc uses, so
+ * calls on different streams are independent except for that one call.
  * Every call is asynchronous on the given stream (a hipStream_t passed as
  * void*, NULL for the default stream) and never synchronises the device.
  *
@@ -82,8 +83,12 @@ enum {
   KVC_E_CAPACITY = -3,  /* clone: dst.max_seq < src.max_seq, or src_len outside [0, src.max_seq] */
   KVC_E_DTYPE = -4,     /* unknown element type, or source and destination types differ */
   KVC_E_WORKSPACE = -5, /* decode workspace missing or smaller than kvc_decode_workspace_bytes */
-  KVC_E_LAUNCH = -6     /* a HIP launch failed */
+  KVC_E_LAUNCH = -6,    /* a HIP launch failed */
+  KVC_E_SCRATCH = -7    /* kvc_attn_decode_noalloc: the call needs more than KVC_DECODE_SCRATCH_MAX_BYTES */
 };
+
+/* Bytes of the static device scratch behind kvc_attn_decode_noalloc (16 MiB). */
+#define KVC_DECODE_SCRATCH_MAX_BYTES ((size_t)16 << 20)
 
 /* Device-side error bits OR-ed into *dev_err. */
 enum {
@@ -177,6 +182,33 @@ size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int
 int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out,
                     int32_t n_q_heads, float scale, int32_t n_workers, void* workspace,
                     size_t workspace_bytes, int32_t* dev_err, void* stream);
+
+/*
+ * kvc_attn_decode_noalloc -- kvc_attn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels, with the partial results in a
+ * static device array of KVC_DECODE_SCRATCH_MAX_BYTES that the library owns
+ * (one copy per device, held until the process ends) instead of a caller
+ * workspace.  It calls no allocating routine.
+ *
+ * Arguments, results and errors are kvc_attn_decode's (output bit-identical
+ * to it for the same inputs and n_workers), except: a call whose
+ * kvc_decode_workspace_bytes(cache, n_q_heads, n_workers) exceeds
+ * KVC_DECODE_SCRATCH_MAX_BYTES returns KVC_E_SCRATCH and launches nothing.
+ * With the default worker count every bfloat16 and int8 cache fits (at most
+ * 8.5 MB at 256 workgroups); a float32 cache needs
+ * batch * n_q_heads * ceil(max_seq / 512) * (head_dim + 2) * 4 bytes once
+ * max_seq exceeds 512.  The array's address on a device is looked up on the
+ * first call made with that device current.
+ *
+ * Every call on one device shares that device's array, and each call
+ * overwrites what the last one left there (no part of it needs to start at
+ * zero).  Calls that overlap in time on one device -- on different streams,
+ * or from different host threads without stream ordering -- race on it and
+ * may return wrong results; calls ordered on one stream are safe.
+ */
+int kvc_attn_decode_noalloc(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out,
+                            int32_t n_q_heads, float scale, int32_t n_workers, int32_t* dev_err, void* stream);
 
 /*
  * kvc_attn_prefill -- T new query tokens per row, causal by absolute position,

@@ -28,13 +28,16 @@ KVC_E_CAPACITY = -3
 KVC_E_DTYPE = -4
 KVC_E_WORKSPACE = -5
 KVC_E_LAUNCH = -6
+KVC_E_SCRATCH = -7
+KVC_DECODE_SCRATCH_MAX_BYTES = 16 << 20  # the static scratch behind kvc_attn_decode_noalloc
 KVC_DEV_CAPACITY = 1
 KVC_DEV_NOT_EMPTY = 2
 KVC_DEV_SRC_LEN = 4
 KVC_DEV_TOKENS = 8
 
 EXPORTS = ("kvc_rope_append", "kvc_rope_append_ragged", "kvc_decode_workspace_bytes", "kvc_attn_decode",
-           "kvc_attn_prefill", "kvc_attn_mixed", "kvc_decode_step", "kvc_prefill_clone", "kvc_status_string")
+           "kvc_attn_decode_noalloc", "kvc_attn_prefill", "kvc_attn_mixed", "kvc_decode_step",
+           "kvc_prefill_clone", "kvc_status_string")
 
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16, torch.int8: KVC_I8}
 
@@ -62,6 +65,8 @@ def _load():
     lib.kvc_decode_workspace_bytes.restype = SZ
     lib.kvc_attn_decode.argtypes = [cp, I32, P, P, I32, F32, I32, P, SZ, P, P]
     lib.kvc_attn_decode.restype = ctypes.c_int
+    lib.kvc_attn_decode_noalloc.argtypes = [cp, I32, P, P, I32, F32, I32, P, P]
+    lib.kvc_attn_decode_noalloc.restype = ctypes.c_int
     lib.kvc_attn_prefill.argtypes = [cp, I32, P, P, I32, I32, F32, P, P]
     lib.kvc_attn_prefill.restype = ctypes.c_int
     lib.kvc_decode_step.argtypes = [cp, I32, P, P, P, P, I32, F32, F32, P, P]
@@ -244,6 +249,20 @@ def kvc_attn_decode(cache: KVCache, layer: int, q_rot, out=None, scale: float = 
                              int(n_workers), _ptr(workspace), ws_bytes, _ptr(dev_err),
                              _stream(stream, cache.k.device))
     _check("kvc_attn_decode", st)
+    return out
+
+
+def kvc_attn_decode_noalloc(cache: KVCache, layer: int, q_rot, out, scale: float = 0.0, n_workers: int = 0,
+                            dev_err=None, stream=None):
+    """kvc_attn_decode with its partial results in the library's static device scratch: the
+    library allocates nothing, and so does this wrapper (`out` is the caller's).  Calls that
+    overlap on one device race on that scratch; calls ordered on one stream do not.  Returns out."""
+    b, t, hq, d = q_rot.shape
+    _like(q_rot, cache, (cache.batch, 1, hq, cache.head_dim), "q_rot")
+    _like(out, cache, q_rot.shape, "out")
+    st = lib.kvc_attn_decode_noalloc(cache.desc(), int(layer), _ptr(q_rot), _ptr(out), int(hq), float(scale),
+                                     int(n_workers), _ptr(dev_err), _stream(stream, cache.k.device))
+    _check("kvc_attn_decode_noalloc", st)
     return out
 
 

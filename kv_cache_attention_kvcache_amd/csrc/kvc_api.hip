@@ -1,5 +1,7 @@
 // The C entry points of libkvc: validate on the host, then launch on the
-// caller's stream.  Nothing here allocates, synchronises or keeps state.
+// caller's stream.  Nothing here allocates or synchronises.  The state kept
+// across calls is per device: the CU count, and the address of the static
+// decode scratch once kvc_attn_decode_noalloc has looked it up.
 #include <math.h>
 #include <stdint.h>
 
@@ -7,6 +9,13 @@
 
 #include "kvc.h"
 #include "kvc_launch.h"
+
+// Scratch of kvc_attn_decode_noalloc: a fixed array in device memory that every
+// call on a device shares (each device holds its own copy for the life of the
+// process).  In host code the array's name is not a device address; its address
+// on the current device is looked up once per device with hipGetSymbolAddress
+// (device_scratch below) and only that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[KVC_DECODE_SCRATCH_MAX_BYTES];
 
 namespace {
 
@@ -122,6 +131,21 @@ size_t decode_ws_bytes(const kvc_cache* c, int32_t n_q_heads, int32_t n_workers)
   return size_t(c->batch) * size_t(n_q_heads) * size_t(max_splits) * size_t(c->head_dim + 2) * sizeof(float);
 }
 
+// The scratch array's address on the current device (null if it cannot be had).
+// Looked up on a device's first kvc_attn_decode_noalloc call, with that device
+// current, then kept.
+void* device_scratch() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<void*> addr[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 int launch_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_E_LAUNCH; }
 
 // Validation and launch shared by the uniform and the ragged append (T: tokens per
@@ -216,6 +240,51 @@ int prefill_f32_impl(const kvc_cache* cache, const kvc::LayerView& lv, const voi
   return launch_status(kvc::launch_split_attention(p, s));
 }
 
+int decode_impl(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out, int32_t n_q_heads, float scale,
+                int32_t n_workers, void* workspace, size_t workspace_bytes, bool static_scratch, int32_t* dev_err,
+                void* stream) {
+  int st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (layer < 0 || layer >= cache->n_layers) return KVC_E_ARG;
+  if (!q_rot || !out || !aligned16(q_rot) || !aligned16(out)) return KVC_E_ARG;
+  if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
+  if (n_workers < 0) return KVC_E_ARG;
+  float sc;
+  if (!resolve_scale(scale, cache->head_dim, &sc)) return KVC_E_ARG;
+  const size_t need = decode_ws_bytes(cache, n_q_heads, n_workers);
+  if (static_scratch) {
+    if (need > KVC_DECODE_SCRATCH_MAX_BYTES) return KVC_E_SCRATCH;
+    if (need > 0) {
+      workspace = device_scratch();
+      workspace_bytes = KVC_DECODE_SCRATCH_MAX_BYTES;
+      if (!workspace) return KVC_E_LAUNCH;
+    }
+  }
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return KVC_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->dtype != KVC_F32)  // bfloat16 or int8 cache
+    return decode_bf16_impl(cache, layer_view(cache, layer), q_rot, out, n_q_heads, sc, n_workers, workspace,
+                            dev_err, s);
+  // float32: split-KV over fixed 512-key splits.
+  kvc::SplitParams p;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.kv = layer_view(cache, layer);
+  p.q = q_rot;
+  p.out = out;
+  p.T = 1;
+  p.n_q_heads = n_q_heads;
+  p.split_keys = kDefaultSplitKeys;
+  p.max_splits = int32_t((int64_t(cache->max_seq) + kDefaultSplitKeys - 1) / kDefaultSplitKeys);
+  p.direct = need == 0;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.direct ? nullptr
+                     : p.ws_o + size_t(cache->batch) * n_q_heads * size_t(p.max_splits) * cache->head_dim;
+  p.dev_err = dev_err;
+  hipError_t e = kvc::launch_split_attention(p, s);
+  if (e == hipSuccess && !p.direct) e = kvc::launch_split_combine(p, s);
+  return launch_status(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,38 +317,13 @@ size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int
 int kvc_attn_decode(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out, int32_t n_q_heads,
                     float scale, int32_t n_workers, void* workspace, size_t workspace_bytes, int32_t* dev_err,
                     void* stream) {
-  int st = check_cache(cache);
-  if (st != KVC_OK) return st;
-  if (layer < 0 || layer >= cache->n_layers) return KVC_E_ARG;
-  if (!q_rot || !out || !aligned16(q_rot) || !aligned16(out)) return KVC_E_ARG;
-  if ((st = check_heads(cache, n_q_heads)) != KVC_OK) return st;
-  if (n_workers < 0) return KVC_E_ARG;
-  float sc;
-  if (!resolve_scale(scale, cache->head_dim, &sc)) return KVC_E_ARG;
-  const size_t need = decode_ws_bytes(cache, n_q_heads, n_workers);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return KVC_E_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (cache->dtype != KVC_F32)  // bfloat16 or int8 cache
-    return decode_bf16_impl(cache, layer_view(cache, layer), q_rot, out, n_q_heads, sc, n_workers, workspace,
-                            dev_err, s);
-  // float32: split-KV over fixed 512-key splits.
-  kvc::SplitParams p;
-  p.scale_log2 = sc * 1.4426950408889634f;
-  p.kv = layer_view(cache, layer);
-  p.q = q_rot;
-  p.out = out;
-  p.T = 1;
-  p.n_q_heads = n_q_heads;
-  p.split_keys = kDefaultSplitKeys;
-  p.max_splits = int32_t((int64_t(cache->max_seq) + kDefaultSplitKeys - 1) / kDefaultSplitKeys);
-  p.direct = need == 0;
-  p.ws_o = static_cast<float*>(workspace);
-  p.ws_ml = p.direct ? nullptr
-                     : p.ws_o + size_t(cache->batch) * n_q_heads * size_t(p.max_splits) * cache->head_dim;
-  p.dev_err = dev_err;
-  hipError_t e = kvc::launch_split_attention(p, s);
-  if (e == hipSuccess && !p.direct) e = kvc::launch_split_combine(p, s);
-  return launch_status(e);
+  return decode_impl(cache, layer, q_rot, out, n_q_heads, scale, n_workers, workspace, workspace_bytes, false,
+                     dev_err, stream);
+}
+
+int kvc_attn_decode_noalloc(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out,
+                            int32_t n_q_heads, float scale, int32_t n_workers, int32_t* dev_err, void* stream) {
+  return decode_impl(cache, layer, q_rot, out, n_q_heads, scale, n_workers, nullptr, 0, true, dev_err, stream);
 }
 
 int kvc_attn_prefill(const kvc_cache* cache, int32_t layer, const void* q_rot, void* out, int32_t T,
@@ -393,6 +437,7 @@ const char* kvc_status_string(int status) {
     case KVC_E_DTYPE: return "unsupported or mismatched element type";
     case KVC_E_WORKSPACE: return "decode workspace missing, misaligned or too small";
     case KVC_E_LAUNCH: return "HIP kernel launch failed";
+    case KVC_E_SCRATCH: return "the call needs more scratch than the library's static decode buffer holds";
     default: return "unknown status";
   }
 }

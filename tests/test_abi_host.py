@@ -33,8 +33,8 @@ def _declared():
 
 def test_header_declares_the_four_calls_and_helpers():
     assert _declared() == sorted(["kvc_rope_append", "kvc_rope_append_ragged", "kvc_decode_workspace_bytes",
-                                  "kvc_attn_decode", "kvc_attn_prefill", "kvc_attn_mixed", "kvc_decode_step",
-                                  "kvc_prefill_clone", "kvc_status_string"])
+                                  "kvc_attn_decode", "kvc_attn_decode_noalloc", "kvc_attn_prefill",
+                                  "kvc_attn_mixed", "kvc_decode_step", "kvc_prefill_clone", "kvc_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -56,7 +56,7 @@ P = ctypes.c_void_p
 
 
 def test_status_strings(lib):
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         s = lib.kvc_status_string(code)
         assert s and s != "unknown status"
     assert lib.kvc_status_string(-99) == "unknown status"
@@ -118,6 +118,32 @@ def test_decode_and_prefill_validation(lib):
     assert L.kvc_attn_prefill(ctypes.byref(d), 0, None, q, 4, 16, 0.0, None, None) == lib.KVC_E_ARG
     assert L.kvc_attn_prefill(ctypes.byref(_desc(lib, head_dim=32)), 0, q, q, 4, 16, 0.0, None,
                               None) == lib.KVC_E_SHAPE
+
+
+def test_noalloc_decode_validation(lib):
+    """kvc_attn_decode_noalloc validates as kvc_attn_decode does, and refuses a call whose partial
+    results would not fit its static scratch -- all before any HIP call."""
+    L = lib.lib
+    d = _desc(lib, max_seq=4096)
+    q = P(0x40000)
+    assert L.kvc_attn_decode_noalloc(ctypes.byref(d), 2, q, q, 16, 0.0, 8, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_decode_noalloc(ctypes.byref(d), 0, None, q, 16, 0.0, 8, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_decode_noalloc(ctypes.byref(d), 0, q, P(0x40004), 16, 0.0, 8, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_decode_noalloc(ctypes.byref(d), 0, q, q, 5, 0.0, 8, None, None) == lib.KVC_E_SHAPE
+    assert L.kvc_attn_decode_noalloc(ctypes.byref(d), 0, q, q, 16, 0.0, -1, None, None) == lib.KVC_E_ARG
+    assert L.kvc_attn_decode_noalloc(ctypes.byref(d), 0, q, q, 16, float("inf"), 8, None, None) == lib.KVC_E_ARG
+    # bfloat16, group 4: 2 partial slots x 4 heads x (128 + 2) floats per workgroup = 4160 B; 4033 workgroups
+    # is the first count past 16 MiB
+    per_wg = 2 * 4 * 130 * 4
+    first_over = lib.KVC_DECODE_SCRATCH_MAX_BYTES // per_wg + 1
+    assert L.kvc_decode_workspace_bytes(ctypes.byref(d), 16, first_over) > lib.KVC_DECODE_SCRATCH_MAX_BYTES
+    assert L.kvc_decode_workspace_bytes(ctypes.byref(d), 16, first_over - 1) <= lib.KVC_DECODE_SCRATCH_MAX_BYTES
+    assert L.kvc_attn_decode_noalloc(ctypes.byref(d), 0, q, q, 16, 0.0, first_over, None,
+                                     None) == lib.KVC_E_SCRATCH
+    # float32: fixed 512-key splits per (row, query head): 64 rows x 16 heads x 2048 splits is far past it
+    f = _desc(lib, max_seq=1 << 20, batch=64, dtype=lib.KVC_F32)
+    assert L.kvc_attn_decode_noalloc(ctypes.byref(f), 0, q, q, 16, 0.0, 0, None, None) == lib.KVC_E_SCRATCH
+    assert "scratch" in lib.kvc_status_string(lib.KVC_E_SCRATCH)
 
 
 def test_clone_validation(lib):
