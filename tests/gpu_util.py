@@ -56,6 +56,15 @@ def make_cache(kvc, n_layers, batch, max_seq, n_kv, d, dtype: str, poison=True):
     return kvc.KVCache(k, v, torch.zeros(batch, dtype=torch.int32, device="cuda"))
 
 
+def _rope_err(got: np.ndarray, ref: np.ndarray, x_in: np.ndarray, dtype: str):
+    half = x_in.shape[-1] // 2
+    pair = np.sqrt(x_in[..., :half] ** 2 + x_in[..., half:] ** 2)
+    pair = np.concatenate([pair, pair], axis=-1)
+    _, e = np.frexp(np.abs(ref))
+    ulp = np.ldexp(1.0, e - (8 if dtype == "bf16" else 24))
+    return np.abs(got - ref), ulp, pair
+
+
 def rope_error_ok(got: np.ndarray, ref: np.ndarray, x_in: np.ndarray, dtype: str) -> bool:
     """Is a rotated vector within the error a float32 rotation can have?
 
@@ -65,9 +74,16 @@ def rope_error_ok(got: np.ndarray, ref: np.ndarray, x_in: np.ndarray, dtype: str
     the storage type at the output, or 2^-20 |(a, b)|, whichever is larger.
     x_in: the unrotated input (..., D) in storage precision.
     """
-    half = x_in.shape[-1] // 2
-    pair = np.sqrt(x_in[..., :half] ** 2 + x_in[..., half:] ** 2)
-    pair = np.concatenate([pair, pair], axis=-1)
-    _, e = np.frexp(np.abs(ref))
-    ulp = np.ldexp(1.0, e - (8 if dtype == "bf16" else 24))
-    return bool(np.all(np.abs(got - ref) <= np.maximum(ulp, pair * 2.0 ** -20)))
+    err, ulp, pair = _rope_err(got, ref, x_in, dtype)
+    return bool(np.all(err <= np.maximum(ulp, pair * 2.0 ** -20)))
+
+
+def rope_excess_ratio(got: np.ndarray, ref: np.ndarray, x_in: np.ndarray, dtype: str):
+    """How close a rotated tensor comes to the 2^-20 |(a, b)| allowance: the largest
+    |got - ref| / |(a, b)| over the elements that are more than one storage ulp off, and how
+    many such elements there are ((0.0, 0) when every element is within an ulp)."""
+    err, ulp, pair = _rope_err(got, ref, x_in, dtype)
+    over = err > ulp
+    if not np.any(over):
+        return 0.0, 0
+    return float(np.max(err[over] / pair[over])), int(np.count_nonzero(over))

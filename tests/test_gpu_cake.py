@@ -1,18 +1,59 @@
 """Cake's bidirectional KV-cache preparation on the GPU (GPU).
 
 Whatever mix of computed and loaded chunks it ends with, the prepared cache
-must be bit-identical to the one chunked prefill computes alone: the stored
-chunks are those the same kernels wrote.
+must be bit-identical to the one chunked prefill computes alone (the stored
+chunks are those the same kernels wrote), and it must hold what the oracle
+says the prompt's cache is: every position's rotated key and value, and a
+decode query over it must see the no-cache attention of the whole prompt.
 """
 import numpy as np
 import pytest
 import torch
 
 from kv_cache_attention_kvcache_amd import cake
-from tests.gpu_util import bits
+from oracle import attention as oatt
+from tests import gates
+from tests.gpu_util import bits, dev, host64, rope_error_ok
 from tests.test_gpu_kernels import _rng
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("gbps", [2.0])
+def test_cake_cache_matches_the_oracle(kvc, gbps):
+    """A Cake-prepared cache (some chunks computed, some loaded) against the oracle: every one of
+    the prompt's positions in every layer holds the oracle's rotated key (within a float32
+    rotation's error) and its value bit for bit, and a decode token appended after it attends
+    exactly the no-cache prompt (Cake paper, Section 4 and Appendix A: either way of producing a
+    chunk's KV cache gives the same cache)."""
+    n, chunk, hq, hkv, d, layers = 6, 256, 16, 4, 128, 2
+    g = _rng(42, n, chunk)
+    raw = [tuple(g.standard_normal((1, chunk, h, d)).astype(np.float32) for h in (hq, hkv, hkv)) for _ in range(n)]
+    chunks = [tuple(dev(x, "bf16") for x in c) for c in raw]
+    ref = kvc.KVCache.empty(layers, 1, n * chunk + 1, hkv, d, dtype=torch.bfloat16)
+    cake.prepare(ref, chunks, None, chunk, mode="compute")
+    store = cake.ThrottledStorage(ref.k.cpu().pin_memory(), ref.v.cpu().pin_memory(), chunk, gbps, "cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = kvc.KVCache.empty(layers, 1, n * chunk + 1, hkv, d, dtype=torch.bfloat16)
+    r = cake.prepare(got, chunks, store, chunk, mode="cake", dev_err=err)
+    assert err.item() == 0 and sorted(r.computed + r.loaded) == list(range(n))
+    q_all, k_all, v_all = (np.concatenate([c[i][0] for c in raw]) for i in range(3))  # (n * chunk, heads, d)
+    k_ref, v_ref = oatt.appended_slots(k_all, v_all, 0, "bf16")
+    k_in = host64(dev(k_all, "bf16"))
+    for layer in range(layers):
+        k_got = host64(got.k[layer, 0, :n * chunk])
+        v_got = host64(got.v[layer, 0, :n * chunk])
+        assert np.array_equal(v_got, v_ref), f"layer {layer}: values differ from the oracle's"
+        assert rope_error_ok(k_got, k_ref, k_in, "bf16"), f"layer {layer}: keys beyond a float32 rotation's error"
+    # one decode token on the prepared cache, against the no-cache oracle over prompt + token
+    t = [g.standard_normal((1, 1, h, d)).astype(np.float32) for h in (hq, hkv, hkv)]
+    q_rot = kvc.kvc_rope_append(got, 1, *(dev(x, "bf16") for x in t), dev_err=err)
+    out = kvc.kvc_attn_decode(got, 1, q_rot, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    want = oatt.nocache_outputs(np.concatenate([q_all, t[0][0]]), np.concatenate([k_all, t[1][0]]),
+                                np.concatenate([v_all, t[2][0]]), [n * chunk], "bf16")
+    gates.check(host64(out)[0], want, "bf16", "decode over the Cake-prepared cache")
 
 
 @pytest.mark.parametrize("gbps", [0.5, 8.0, 1000.0])

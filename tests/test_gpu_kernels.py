@@ -283,6 +283,34 @@ def test_decode_batch_row_equals_single_row_run(kvc):
         gates.check(single, ref[b], dtype, f"row {b} alone vs oracle")
 
 
+def test_decode_on_a_side_stream_with_the_binding_workspace(kvc):
+    """workspace=None and out=None on a stream other than the current one: the binding's temporary
+    buffers are recorded on that stream, so the default stream's allocations made while the decode
+    still runs cannot take their memory.  Every output must match the oracle."""
+    dtype, hq, hkv, d = "bf16", 64, 8, 128
+    lengths = [4000, 3000, 4095, 2500]
+    g = _rng(9, hq, d)
+    cache = make_cache(kvc, 2, len(lengths), max(lengths) + 1, hkv, d, dtype)
+    hist_k, hist_v = _fill_prefix(cache, 1, lengths, dtype, g)
+    q = g.standard_normal((len(lengths), 1, hq, d)).astype(np.float32)
+    k = g.standard_normal((len(lengths), 1, hkv, d)).astype(np.float32)
+    v = g.standard_normal((len(lengths), 1, hkv, d)).astype(np.float32)
+    q_rot = kvc.kvc_rope_append(cache, 1, dev(q, dtype), dev(k, dtype), dev(v, dtype))
+    ref = np.stack([oatt.decode_over_existing(hist_k[b], hist_v[b], q[b, 0], k[b, 0], v[b, 0], dtype)
+                    for b in range(len(lengths))])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs, churn = [], []
+    for _ in range(6):
+        outs.append(kvc.kvc_attn_decode(cache, 1, q_rot, stream=side))  # the binding allocates both buffers
+        # meanwhile the default stream allocates and poisons memory of the freed workspace's size
+        churn.append(torch.full((kvc.kvc_decode_workspace_bytes(cache, hq) // 4,), float("nan"), device="cuda"))
+        del churn[0]
+    torch.cuda.synchronize()
+    for i, out in enumerate(outs):
+        gates.check(host64(out)[:, 0], ref, dtype, f"side-stream decode {i}")
+
+
 def test_decode_capacity_and_workspace_errors(kvc):
     dtype = "bf16"
     cache = make_cache(kvc, 1, 2, 1024, 4, 128, dtype)
