@@ -16,7 +16,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvc.so")
+# KVC_LIB_PATH selects another build of the same library (the host-sanitizer build the CPU tests use)
+LIB_PATH = os.environ.get("KVC_LIB_PATH") or os.path.join(_HERE, "libkvc.so")
 
 KVC_F32 = 0
 KVC_BF16 = 1

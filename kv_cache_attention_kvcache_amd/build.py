@@ -58,6 +58,50 @@ def _link(objs, path: str) -> None:
     os.replace(tmp, path)
 
 
+# The host side of the C entry points (argument validation, dispatch) under AddressSanitizer and
+# UndefinedBehaviorSanitizer.  Only host code is instrumented: each -fsanitize= sits behind
+# -Xarch_host, so the device code is the same as in libkvc.so.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_DIR = os.path.join(BUILD_DIR, "sanitize")
+SAN_LIB_PATH = os.path.join(SAN_DIR, "libkvc.so")
+
+
+def asan_runtime() -> str:
+    """The ASan runtime of the ROCm compiler, which a process must preload to load the sanitized library."""
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("the ROCm compiler's ASan runtime is not installed")
+    return found[-1]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libkvc.so with its host code under ASan + UBSan, in _build/sanitize/; returns its path."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+    def compile_one(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *FLAGS, *SANITIZE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    tmp = SAN_LIB_PATH + f".tmp{os.getpid()}"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE_FLAGS, "-shared-libsan", *objs,
+           "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stderr}")
+    os.replace(tmp, SAN_LIB_PATH)
+    if verbose:
+        print(f"built {SAN_LIB_PATH}")
+    return SAN_LIB_PATH
+
+
 def build(verbose: bool = False) -> str:
     """Compile every kernel source, link libkvc.so and libkvc_ceilings.so; returns libkvc's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)

@@ -38,7 +38,7 @@ def test_header_declares_the_four_calls_and_helpers():
 
 
 def test_every_declared_symbol_is_exported(lib):
-    raw = ctypes.CDLL(LIB)
+    raw = ctypes.CDLL(lib.LIB_PATH)  # the build the binding loaded (KVC_LIB_PATH may select another)
     for name in _declared():
         assert hasattr(raw, name), name
     assert set(_declared()) == set(lib.EXPORTS)
