@@ -956,8 +956,12 @@ __global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p
   const int count = w_last - w_first + 1;
   const int slot0 = range_begin(w_first, n_tiles, p.n_wg) == base ? 0 : 1;
   auto part = [&](int i) { return (size_t(w_first + i) * 2 + (i == 0 ? slot0 : 0)) * GB + h; };
+  // With at least as many tiles as workgroups every workgroup holds a tile, so none of
+  // w_first..w_last is empty and the check (two 64-bit divisions per partial) is skipped.
+  const bool may_be_empty = n_tiles < p.n_wg;
   auto empty = [&](int i) {
-    return range_begin(w_first + i, n_tiles, p.n_wg) == range_begin(w_first + i + 1LL, n_tiles, p.n_wg);
+    return may_be_empty &&
+           range_begin(w_first + i, n_tiles, p.n_wg) == range_begin(w_first + i + 1LL, n_tiles, p.n_wg);
   };
 
   float mx = -INFINITY;
