@@ -101,7 +101,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", choices=["long_context", "long_context_int8", "tiny", "cake", "mixed", "ragged_b64",
-                                           "gqa_clone", "clocks"],
+                                           "gqa_clone", "clocks", "clone"],
                     default="long_context")
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
@@ -161,6 +161,8 @@ def main():
         return bench_gqa_clone(args)
     if args.workload == "clocks":
         return bench_clocks(args)
+    if args.workload == "clone":
+        return bench_clone(args)
     import kv_cache_attention_kvcache_amd as kvc
     import synth
 
@@ -815,6 +817,67 @@ def cpu_baseline_gqa(w, n_prompt, rows, n_dec, quiet):
             "tokens_per_s": round(done / dt, 2),
             "sample": f"{done} no-cache decode calls of row 0, cycling steps {steps} (each re-rotating the "
                       f"2000-token prompt and the steps so far), {dt:.1f} s"}
+
+
+def bench_clone(args):
+    """The batch-1 -> batch-8 clone of the 73,728-token prompt's cache, beside a plain fill that
+    writes the same destination bytes; one JSON line.
+
+    64 q / 8 kv heads, head_dim 128, bf16, max_seq 74,240 (nanochat post, "The prefill trick, 12
+    lines").  The clone reads the 0.30 GB source once and writes 2.42 GB; the fill (torch's own
+    fill kernel over the same destination slices) writes the 2.42 GB and reads nothing, so it shows
+    the write rate this pattern of destination rows allows.  Also the launch sequence the clone's
+    counter runs profile.
+    """
+    import kv_cache_attention_kvcache_amd as kvc
+    import synth
+
+    w = synth.LONG_CONTEXT
+    ctx, hkv, d, rows = w.extra["context"], w.n_kv_heads, w.head_dim, w.extra["clone_rows"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    src = kvc.KVCache.empty(1, 1, w.max_seq, hkv, d, dtype=torch.bfloat16, device=dev)
+    src.k.normal_(generator=gen)
+    src.v.normal_(generator=gen)
+    src.seqlens.fill_(ctx)
+    dst = kvc.KVCache.empty(1, rows, w.max_seq, hkv, d, dtype=torch.bfloat16, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    K = max(1, args.steps) + 2
+    t_clone, t_fill = Timer(), Timer()
+    for i in range(K + 1):
+        dst.seqlens.zero_()
+        with t_clone if i > 0 else _Null():
+            kvc.kvc_prefill_clone(src, ctx, dst, dev_err=err)
+    for i in range(K + 1):
+        with t_fill if i > 0 else _Null():
+            dst.k[:, :, :ctx].fill_(1.0)
+            dst.v[:, :, :ctx].fill_(1.0)
+    torch.cuda.synchronize()
+    assert err.item() == 0, f"device error bits {err.item()}"
+    if args.copy_probe_mib > 0:  # a known-size copy that calibrates the profiler's byte counters
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        torch.empty_like(a).copy_(a)
+        torch.cuda.synchronize()
+    tok = 2 * hkv * d * 2
+    nbytes = ctx * tok * (1 + rows)
+    med = lambda t: sorted(t.times_ms())[len(t.times_ms()) // 2]
+    gbps = nbytes / (med(t_clone) * 1e-3) / 1e9
+    fill_gbps = ctx * tok * rows / (med(t_fill) * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "prefill clone GB/s (source read once + every row written)", "value": round(gbps, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": 1, "ms_per_step": round(med(t_clone), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name + "_clone", "context": ctx, "rows": rows, "kv_heads": hkv, "head_dim": d,
+                   "parallelism": "none"},
+        "clone_us": round(med(t_clone) * 1e3, 1), "fill_same_bytes_us": round(med(t_fill) * 1e3, 1),
+        "fill_write_gbps": round(fill_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "clone_copy_kernel", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("clone_b8_72k"), "bytes_per_launch": nbytes,
+                     "avg_launch_us": round(med(t_clone) * 1e3, 1)}}), flush=True)
 
 
 def bench_clocks(args):

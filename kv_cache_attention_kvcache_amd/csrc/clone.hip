@@ -4,9 +4,15 @@
 // contiguous run of src_len * n_kv_heads * head_dim elements, and so is the
 // same run of each destination row.  The copy kernel reads each 16-byte
 // vector of the source run once and writes it to every empty destination
-// row (read once, write N times: HBM-bound).  A second, one-workgroup kernel
-// then sets the destination lengths, so no block reads a length another
-// block may already have changed.  An int8 cache also has one float32 scale
+// row (read once, write N times: HBM-bound).  Its grid has one thread per
+// source vector (no grid-stride loop unless the grid would pass 2^31
+// workgroups), so the workgroups in flight at any moment cover a narrow,
+// advancing stretch of each row: the writes sweep every row in address
+// order.  A persistent grid whose threads stride over the whole run spread
+// the writes over the full 2.4 GB at once and wrote 10% slower (measured on
+// MI355X: 552 against about 500 us for 8 rows of a 73,728-token cache).
+// A second, one-workgroup kernel then sets the destination lengths, so no
+// block reads a length another block may already have changed.  An int8 cache also has one float32 scale
 // per (KV head, position) for K and for V, head-major: per layer, each KV
 // head's positions [0, src_len) are one run, copied the same way (grid planes
 // 2 and 3), 4 bytes at a time.
@@ -73,8 +79,8 @@ hipError_t launch_clone(const CloneParams& p, hipStream_t s) {
   const size_t esz = p.src.dtype == KVC_F32 ? 4 : p.src.dtype == KVC_BF16 ? 2 : 1;
   const size_t n_vec = size_t(p.src_len) * p.src.n_kv_heads * p.src.head_dim * esz / 16;
   if (n_vec > 0) {
-    const size_t want = (n_vec + 255) / 256;
-    const unsigned gx = unsigned(want < 1024 ? want : 1024);
+    const size_t want = (n_vec + 255) / 256;  // one thread per source vector
+    const unsigned gx = unsigned(want < 0x7fffffffu ? want : 0x7fffffffu);
     const unsigned planes = p.src.dtype == KVC_I8 ? 4 : 2;  // K, V (and their scales)
     hipLaunchKernelGGL(clone_copy_kernel, dim3(gx, p.n_layers, planes), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
