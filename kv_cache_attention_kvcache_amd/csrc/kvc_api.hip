@@ -218,6 +218,7 @@ int prefill_bf16_impl(const kvc_cache* cache, const kvc::LayerView& lv, const vo
   p.n_q_heads = n_q_heads;
   p.scale_log2 = sc * 1.4426950408889634f;
   p.dev_err = dev_err;
+  p.n_cus = default_decode_workers();  // the CU count (0 if unknown: 8-wave workgroups)
   return launch_status(kvc::launch_prefill_mfma(p, s));
 }
 

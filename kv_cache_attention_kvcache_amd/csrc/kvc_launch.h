@@ -121,6 +121,7 @@ struct PrefillParams {
   int32_t T, n_q_heads;
   float scale_log2;
   int32_t* dev_err;
+  int32_t n_cus;  // compute units of the device: a grid smaller than this takes 4-wave workgroups
 };
 hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t s);
 

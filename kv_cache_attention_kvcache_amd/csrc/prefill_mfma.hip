@@ -38,8 +38,6 @@ namespace kvc {
 
 namespace {
 
-constexpr int kThreads = 512;  // 8 waves per workgroup
-constexpr int kBM = 256;  // queries per workgroup (8 waves x 32)
 constexpr int kBN = 64;   // keys per tile
 constexpr int kWQ = 32;   // queries per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data format (gfx9 family)
@@ -61,8 +59,14 @@ __device__ __forceinline__ int perm_row(int i) {
   return ((i >> 4) << 4) | (((i >> 2) & 1) << 3) | (((i >> 3) & 1) << 2) | (i & 3);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams p) {
+// WAVES = 8: 256 queries per workgroup, one workgroup per CU (two waves per SIMD).
+// WAVES = 4: 128 queries per workgroup, for calls whose 8-wave grid has fewer
+// workgroups than the device has CUs (a short prompt at few heads): twice the
+// workgroups, so more CUs have work.  Same tiles, pipeline and register budget.
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void prefill_mfma_kernel(PrefillParams p) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kBM = kWQ * WAVES;            // queries per workgroup
   constexpr int kKStride = D * 2 + 16;        // bytes per K row in LDS
   constexpr int kVStride = kBN * 2 + 16;      // bytes per transposed V row (one head dim)
   constexpr int kKD = D / 16;                 // MFMA k-steps over the head dim
@@ -150,16 +154,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
   const bf16_t* v_base = static_cast<const bf16_t*>(p.kv.v) + size_t(b) * p.kv.max_seq * key_stride + size_t(g) * D;
 
   // Staging roles.  K: thread loads 16-byte chunks f = tid + kThreads i of the tile.
-  // V: thread owns keys 2 kq, 2 kq + 1 and head dims 8 dc .. 8 dc + 7.
+  // V: thread owns keys 2 kq, 2 kq + 1 and, for each u < kVPer, head dims
+  // 8 dc_u .. 8 dc_u + 7 with dc_u = dc + (kThreads / 32) u.
   // Loads are range-checked buffer loads whose descriptor starts at the tile's
   // first key: keys at or past kend_wg read as zeros, with no branch.
+  constexpr int kDcStep = kThreads / 32;                      // head-dim groups staged side by side
+  constexpr int kVPer = (D / 8 + kDcStep - 1) / kDcStep;      // groups per thread
   const int kq = tid & 31;
   const int dc = tid >> 5;
-  const bool v_active = dc < D / 8;
   const int row_bytes = hkv * D * 2;
   const int k_off = (tid / (D / 8)) * row_bytes + (tid % (D / 8)) * 16;  // + i * (kThreads / (D/8)) rows
-  const int v_off = 2 * kq * row_bytes + dc * 16;                         // + r rows
-  uint4 kreg[kKLoads], vreg[2];
+  const int v_off = 2 * kq * row_bytes + dc * 16;                         // + r rows, + 16 kDcStep u bytes
+  uint4 kreg[kKLoads], vreg[kVPer][2];
   auto tile_rsrc = [&](const bf16_t* base, int kb0) {
     const int left = (kend_wg - kb0 - 1) * row_bytes + D * 2;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base) + size_t(kb0) * key_stride, (short)0,
@@ -173,12 +179,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
                                               rk, k_off + i * (kThreads / (D / 8)) * row_bytes, 0, 0));
   };
   auto load_v = [&](int tile) {
-    if (v_active) {
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v_base, tile * kBN);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(v_base, tile * kBN);
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
-        vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + r * row_bytes, 0, 0));
-    }
+    for (int u = 0; u < kVPer; ++u)
+      if (dc + kDcStep * u < D / 8) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          vreg[u][r] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + 16 * kDcStep * u + r * row_bytes, 0, 0));
+      }
   };
   auto store_k = [&](int buf) {
 #pragma unroll
@@ -190,12 +199,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
     }
   };
   auto store_v = [&](int buf) {  // transposed: V^T rows are head dims
-    if (v_active) {
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) {
+      const int dcu = dc + kDcStep * u;
+      if (dcu >= D / 8) continue;
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        const int u = dd >> 1;
-        const uint32_t w0 = u4_get(vreg[0], u), w1 = u4_get(vreg[1], u);
-        *reinterpret_cast<uint32_t*>(v_lds[buf] + (8 * dc + dd) * kVStride + 4 * kq) =
+        const int e = dd >> 1;
+        const uint32_t w0 = u4_get(vreg[u][0], e), w1 = u4_get(vreg[u][1], e);
+        *reinterpret_cast<uint32_t*>(v_lds[buf] + (8 * dcu + dd) * kVStride + 4 * kq) =
             (dd & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
       }
     }
@@ -392,15 +404,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillParams
 
 }  // namespace
 
-hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t s) {
-  const int n_qt = (p.T + kBM - 1) / kBM;
+template <int WAVES>
+hipError_t launch_waves(const PrefillParams& p, hipStream_t s) {
+  const int n_qt = (p.T + kWQ * WAVES - 1) / (kWQ * WAVES);
   const long long n_wg = (long long)n_qt * p.n_q_heads * p.kv.batch;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.kv.head_dim == 128)
-    hipLaunchKernelGGL((prefill_mfma_kernel<128>), dim3(unsigned(n_wg)), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<128, WAVES>), dim3(unsigned(n_wg)), dim3(64 * WAVES), 0, s, p);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<64>), dim3(unsigned(n_wg)), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<64, WAVES>), dim3(unsigned(n_wg)), dim3(64 * WAVES), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_mfma(const PrefillParams& p, hipStream_t s) {
+  // 8-wave workgroups unless their grid would leave CUs without a workgroup.
+  const long long n_wg8 = (long long)((p.T + kWQ * 8 - 1) / (kWQ * 8)) * p.n_q_heads * p.kv.batch;
+  return n_wg8 < p.n_cus ? launch_waves<4>(p, s) : launch_waves<8>(p, s);
 }
 
 }  // namespace kvc
