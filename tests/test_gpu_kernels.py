@@ -373,6 +373,36 @@ def test_prefill_matches_oracle(kvc, dtype, hq, hkv, d, t_len, start):
         gates.check(o[b], ref, dtype, f"prefill row {b} start {s}")
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(64, 8, 128), (64, 16, 64)])
+def test_prefill_four_and_eight_wave_forms_agree(kvc, hq, hkv, d):
+    """A batch of 8 rows at 64 query heads takes the 8-wave prefill (its grid fills the device);
+    each row prefilled alone takes the 4-wave form (128 query tiles of 128, fewer workgroups than
+    CUs).  Every query's output is computed by one wave in the same order in both, so the rows
+    must agree bit for bit, and both with the oracle.  T = 300 leaves a ragged last tile."""
+    dtype, batch, t_len = "bf16", 8, 300
+    g = _rng(8, hq, d)
+    starts = [0, 5, 64, 129, 300, 511, 700, 1000]
+    max_seq = max(starts) + t_len + 3
+    cache = make_cache(kvc, 1, batch, max_seq, hkv, d, dtype)
+    hist_k, hist_v = _fill_prefix(cache, 0, starts, dtype, g)
+    q = g.standard_normal((batch, t_len, hq, d)).astype(np.float32)
+    k = g.standard_normal((batch, t_len, hkv, d)).astype(np.float32)
+    v = g.standard_normal((batch, t_len, hkv, d)).astype(np.float32)
+    q_rot = kvc.kvc_rope_append(cache, 0, dev(q, dtype), dev(k, dtype), dev(v, dtype))
+    together = bits(kvc.kvc_attn_prefill(cache, 0, q_rot))
+    for b, s in enumerate(starts):
+        one = kvc.KVCache(cache.k[:, b:b + 1].contiguous(), cache.v[:, b:b + 1].contiguous(),
+                          cache.seqlens[b:b + 1].clone())
+        alone = kvc.kvc_attn_prefill(one, 0, q_rot[b:b + 1].contiguous())
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(alone)[0], together[b]), f"row {b}: 4-wave and 8-wave forms differ"
+        k_new, v_new = oatt.appended_slots(k[b], v[b], s, dtype)
+        ka = np.concatenate([hist_k[b], k_new])
+        va = np.concatenate([hist_v[b], v_new])
+        qh = rope.rotate_round(numerics.round_to(q[b], dtype), np.arange(s, s + t_len), dtype)
+        gates.check(host64(alone)[0], oatt.attend(qh, ka, va, np.arange(s, s + t_len)), dtype, f"row {b}")
+
+
 def test_prefill_chunked_equals_one_shot(kvc):
     """512 tokens in 4 chunks of 128 vs one pass (Cake paper, Section 3): same outputs within tolerance."""
     dtype, hq, hkv, d, n = "bf16", 16, 4, 128, 512
