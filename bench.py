@@ -31,7 +31,14 @@ computes on being random.
 `--workload long_context_int8` runs the same decode steps on an int8 cache
 (codes plus one float32 scale per cached vector): the 72K context is written
 by the quantizing append alone (prefill attention reads bfloat16 caches
-only), then cloned and decoded as above.
+only), then cloned and decoded as above.  Unless --no-ceilings, it then reads
+the final batch-8 cache with no arithmetic (whole head rows straight into LDS)
+in the decode kernel's own assignment and with all heads of a key range per
+workgroup, and reports both rates beside the decode's.
+
+`--workload clone` times the batch-1 -> batch-8 clone of the 72K cache beside a
+fill of the same destination bytes and, unless --no-ceilings, a contiguous
+streaming write of that many bytes.
 
 `--workload cake` prepares the 72K prompt's KV cache Cake's way (chunked
 prefill from the front while a throttled host link loads stored chunks from
@@ -704,6 +711,17 @@ def bench_int8(args):
     total = K * (dec_bytes[1] + dec_bytes[rows]) / ((ms[1] + ms[rows]) * 1e-3) / 1e9
     per_launch = dec_bytes[rows] / n_dec
     avg_ms = ms[rows] / (K * n_dec)
+    probes = None
+    if not args.no_ceilings:  # the same cache read with no arithmetic, in two assignments
+        from kv_cache_attention_kvcache_amd import ceilings
+
+        n_keys = int(cache8.seqlens.min())
+        seg = max(1, torch.cuda.get_device_properties(dev).multi_processor_count // (rows * hkv))
+        probes = ceilings.measure_q8(cache8.k[0], cache8.v[0], cache8.k_scale[0], cache8.v_scale[0], n_keys,
+                                     parts=tuple(sorted({seg, 16, 64})))
+        probes["decode_parts_per_segment"] = seg
+        probes["n_keys"] = n_keys
+        log(f"int8 read probes: {probes}", args.quiet)
     if args.copy_probe_mib > 0:  # a known-size copy that calibrates the profiler's byte counters
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -727,7 +745,11 @@ def bench_int8(args):
                      "traffic": measured_traffic("decode_q8_b8_72k"), "bytes_per_launch": int(per_launch),
                      "avg_launch_us": round(avg_ms * 1e3, 2),
                      "note": "codes + float32 scales per launch; the products run on bf16 matrix cores, "
-                             "one workgroup per CU and one tile in flight per wave"},
+                             "one workgroup per CU and one tile in flight per wave",
+                     **({"measured_ceiling": probes["q8_read_segments_gbps"][str(probes["decode_parts_per_segment"])],
+                         "measured_ceiling_probe": "q8_read_segments_gbps at the decode's own parts per segment"}
+                        if probes else {})},
+        **({"read_probes": probes} if probes else {}),
         **({"cpu_baseline": cpu} if cpu else {})}),
           flush=True)
 
@@ -934,6 +956,13 @@ def bench_clone(args):
         torch.cuda.synchronize()
     tok = 2 * hkv * d * 2
     nbytes = ctx * tok * (1 + rows)
+    write_probe = None
+    if not args.no_ceilings:  # one contiguous buffer of the bytes the clone writes, written in address order
+        from kv_cache_attention_kvcache_amd import ceilings
+
+        wbuf = torch.empty(ctx * tok * rows, dtype=torch.uint8, device=dev)
+        write_probe = ceilings.measure_write(wbuf)
+        del wbuf
     med = lambda t: sorted(t.times_ms())[len(t.times_ms()) // 2]
     gbps = nbytes / (med(t_clone) * 1e-3) / 1e9
     fill_gbps = ctx * tok * rows / (med(t_fill) * 1e-3) / 1e9
@@ -945,6 +974,7 @@ def bench_clone(args):
                    "parallelism": "none"},
         "clone_us": round(med(t_clone) * 1e3, 1), "fill_same_bytes_us": round(med(t_fill) * 1e3, 1),
         "fill_write_gbps": round(fill_gbps, 1),
+        **({"write_probe_gbps": write_probe} if write_probe else {}),
         "roofline": {"bound": "hbm", "kernel": "clone_copy_kernel", "achieved": round(gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic("clone_b8_72k"), "bytes_per_launch": nbytes,

@@ -14,7 +14,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc_ceilings.so")
-EXPORTS = ("kvc_ceiling_stream_read", "kvc_ceiling_mfma_bf16", "kvc_ceiling_lds_read", "kvc_ceiling_decode_read")
+EXPORTS = ("kvc_ceiling_stream_read", "kvc_ceiling_mfma_bf16", "kvc_ceiling_lds_read", "kvc_ceiling_decode_read",
+           "kvc_ceiling_q8_read", "kvc_ceiling_stream_write")
 MFMA_FLOPS = 32768  # one 32x32x16 product: 2 * 32 * 32 * 16 flops
 
 _lib = None
@@ -37,6 +38,10 @@ def _load():
         lib.kvc_ceiling_decode_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         lib.kvc_ceiling_decode_read.restype = ctypes.c_int
+        lib.kvc_ceiling_q8_read.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 2
+        lib.kvc_ceiling_q8_read.restype = ctypes.c_int
+        lib.kvc_ceiling_stream_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.kvc_ceiling_stream_write.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -89,6 +94,40 @@ def decode_read(k: torch.Tensor, v: torch.Tensor, rows: int, n_keys: int, heads:
     if rc != 0:
         raise RuntimeError(f"kvc_ceiling_decode_read failed ({rc})")
     return 2 * need
+
+
+def q8_read(k: torch.Tensor, v: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor, n_keys: int,
+            mode: int, parts: int, sink: torch.Tensor) -> int:
+    """Launch the int8 cache read over keys [0, n_keys) of every row of k, v (int8 or uint8,
+    (rows, max_seq, heads, 128)) and their float32 scales (rows, heads, max_seq); mode 0 reads
+    in the decode kernel's assignment, mode 1 all heads of a key range per workgroup.  Returns
+    the bytes it reads."""
+    rows, max_seq, heads, d = k.shape
+    if d != 128 or tuple(v.shape) != tuple(k.shape) or tuple(k_scale.shape) != (rows, heads, max_seq) or \
+            tuple(v_scale.shape) != tuple(k_scale.shape):
+        raise ValueError("k, v must be (rows, max_seq, heads, 128) and the scales (rows, heads, max_seq)")
+    for t in (k, v, k_scale, v_scale):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("every operand must be a contiguous device tensor")
+    if k.element_size() != 1 or k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
+        raise ValueError("codes are one byte, scales float32")
+    rc = _load().kvc_ceiling_q8_read(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                     ctypes.c_void_p(k_scale.data_ptr()), ctypes.c_void_p(v_scale.data_ptr()),
+                                     rows, n_keys, max_seq, heads, mode, parts, ctypes.c_void_p(sink.data_ptr()),
+                                     _stream_ptr())
+    if rc != 0:
+        raise RuntimeError(f"kvc_ceiling_q8_read failed ({rc})")
+    return 2 * rows * n_keys * heads * (128 + 4)
+
+
+def stream_write(buf: torch.Tensor, nbytes: int) -> int:
+    """Launch the streaming write over the first nbytes of buf (a contiguous uint8 device tensor)."""
+    if buf.dtype != torch.uint8 or not buf.is_cuda or not buf.is_contiguous() or nbytes > buf.numel():
+        raise ValueError("buf must be a contiguous uint8 device tensor of at least nbytes")
+    rc = _load().kvc_ceiling_stream_write(ctypes.c_void_p(buf.data_ptr()), nbytes, _stream_ptr())
+    if rc != 0:
+        raise RuntimeError(f"kvc_ceiling_stream_write failed ({rc})")
+    return nbytes
 
 
 def _timed(fn, reps: int) -> float:
@@ -180,3 +219,31 @@ def measure(device=None, buffer_gib: int = 4, reps: int = 5, decode_shape=(8, 73
         shapes["lds_read_tbps"]["value"] = round(best, 1)
         shapes["lds_read_tbps"]["bytes_per_clk_per_cu"] = round(best * 1e12 / cus / 2.4e9, 1)
     return shapes
+
+
+def measure_q8(k: torch.Tensor, v: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor, n_keys: int,
+               parts=(4, 16, 64), reps: int = 5) -> dict:
+    """Read rates (GB/s) of an int8 cache of the caller's shape, whole head rows landing in LDS:
+
+    * q8_read_segments_gbps: one key range of one (row, KV head) segment per
+      workgroup, for each count of ranges per segment in `parts` (the decode
+      kernel's own assignment is one of them: its persistent grid of one
+      workgroup per CU cut into segments);
+    * q8_read_all_heads_gbps: one key range of a row per workgroup with every
+      KV head of it, so the four waves read whole key rows (heads * 128 bytes)
+      at a time; the best of 64, 128 and 256 ranges per row.
+    """
+    sink = torch.zeros(4, dtype=torch.int32, device=k.device)
+    nbytes = 2 * k.shape[0] * n_keys * k.shape[2] * 132
+    rate = lambda mode, pp: nbytes / _timed(lambda: q8_read(k, v, k_scale, v_scale, n_keys, mode, pp, sink),
+                                            reps) / 1e9
+    seg = {str(pp): round(rate(0, pp), 1) for pp in parts}
+    allh = {str(pp): round(rate(1, pp), 1) for pp in (64, 128, 256)}
+    return {"q8_read_segments_gbps": seg, "q8_read_all_heads_gbps": {"value": max(allh.values()), "by_parts": allh}}
+
+
+def measure_write(buf: torch.Tensor, reps: int = 5) -> float:
+    """Rate (GB/s) of the streaming write over all of buf, one 16-byte store per thread."""
+    n = buf.numel() // 16 * 16
+    t = _timed(lambda: stream_write(buf, n), reps)
+    return round(n / t / 1e9, 1)

@@ -55,6 +55,22 @@ int kvc_ceiling_mfma_bf16(int32_t iters, int32_t chains, int32_t random_operands
 // only for an impossible XOR.  Bytes read per call = workgroups * 8 * iters * 16384.
 int kvc_ceiling_lds_read(int32_t iters, int32_t workgroups, uint32_t* sink, hipStream_t stream);
 
+// Reads an int8 KV cache -- codes (rows, max_seq, heads, 128 bytes) for K and for V, and
+// float32 scales (rows, heads, max_seq) for each, all caller-owned device memory, the code
+// buffers 16-byte aligned -- over keys [0, n_keys) of every row, with whole 128-byte rows
+// loaded straight into LDS (buffer_load_dwordx4 ... lds) one 32-key tile per wave at a time
+// and no arithmetic but an XOR written to *sink only for an impossible value.  mode 0: the
+// decode kernel's assignment, rows * heads * parts workgroups, each one key range of one
+// (row, head).  mode 1: all heads of a key range, rows * parts workgroups, wave h reading
+// heads 2h and 2h + 1 (heads <= 8).  Bytes read per call = 2 * rows * n_keys * heads * (128 + 4).
+int kvc_ceiling_q8_read(const void* k, const void* v, const float* k_scale, const float* v_scale, int32_t rows,
+                        int32_t n_keys, int32_t max_seq, int32_t heads, int32_t mode, int32_t parts, uint32_t* sink,
+                        hipStream_t stream);
+
+// Writes `bytes` (a multiple of 16) of the 16-byte aligned device buffer, one 16-byte store
+// per thread, workgroups in address order.  Bytes written per call = bytes.
+int kvc_ceiling_stream_write(void* buf, int64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -164,6 +164,101 @@ __global__ __launch_bounds__(kLdsThreads) void lds_read_kernel(int32_t iters, ui
   if (acc == kNeverXor) sink[0] = acc;
 }
 
+// Reads of an int8 cache: codes (rows, max_seq, heads, 128 bytes) for K and for V, and
+// float32 scales (rows, heads, max_seq) for each, of keys [0, n_keys) of every row.
+// Whole 128-byte rows are loaded straight into per-wave LDS (buffer_load_dwordx4 ... lds,
+// eight lanes per row), one 32-key tile at a time per wave; the buffers' range checks
+// return zeros past a row's keys.  The data are folded into an XOR written to *sink only
+// for an impossible value, so nothing can be removed.  Each wave waits for its own loads
+// (vmcnt) before it touches its stage.
+constexpr int kQ8Tile = 32;
+constexpr int kQ8Stage = 8 * 1024 + 512;  // K codes, V codes, K scales, V scales of one tile
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ void q8_wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// One tile of one head: 32 key rows of 128 bytes at a `row_bytes` stride from k_head/v_head,
+// and the head's 32 scales, into `stage`.
+__device__ __forceinline__ void q8_issue(uint8_t* stage, const uint8_t* k_head, const uint8_t* v_head,
+                                         const float* ks_head, const float* vs_head, int key0, int n_keys,
+                                         int row_bytes, int lane) {
+  const int left = (n_keys - key0 - 1) * row_bytes + 128;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(k_head) + size_t(key0) * row_bytes, (short)0, left > 0 ? left : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(v_head) + size_t(key0) * row_bytes, (short)0, left > 0 ? left : 0, 0x00020000);
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int off = (8 * n + lane / 8) * row_bytes + 16 * (lane % 8);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(stage + 1024 * n), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(stage + 4096 + 1024 * n), 16, off, 0, 0, 0);
+  }
+  const int sleft = (n_keys - key0) * 4;  // lanes 32..63 read past the tile's scales: zeros or the next keys'
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ks_head) + key0, (short)0,
+                                                                      sleft > 0 ? sleft : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(vs_head) + key0, (short)0,
+                                                                      sleft > 0 ? sleft : 0, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(stage + 8192), 4, 4 * lane, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_ptr)(stage + 8192 + 256), 4, 4 * lane, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t q8_use(const uint8_t* stage, int lane) {
+  q8_wait_all();
+  const uint32_t a = *reinterpret_cast<const uint32_t*>(stage + 16 * lane) ^
+                     *reinterpret_cast<const uint32_t*>(stage + 4096 + 16 * lane) ^
+                     *reinterpret_cast<const uint32_t*>(stage + 8192 + 4 * lane);
+  __builtin_amdgcn_s_waitcnt(0);  // the stage's reads are done before the next loads land in it
+  return a;
+}
+
+// mode 0, the decode kernel's assignment: workgroup w streams key range w % parts of segment
+// (row, head) = divmod(w / parts, heads); its four waves take the range's tiles in turn.
+// mode 1, all heads of a key range: workgroup w streams key range w % parts of row w / parts,
+// wave h taking heads 2h and 2h + 1 of every tile, so the four waves read whole key rows.
+__global__ __launch_bounds__(kThreads) void q8_read_kernel(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                                                          const float* __restrict__ ks, const float* __restrict__ vs,
+                                                          int32_t n_keys, int32_t max_seq, int32_t heads, int32_t mode,
+                                                          int32_t parts, uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t stages[4][kQ8Stage];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
+  const int row_bytes = heads * 128;
+  const int nt = (n_keys + kQ8Tile - 1) / kQ8Tile;
+  uint8_t* stage = stages[wave];
+  uint32_t acc = 0;
+  if (mode == 0) {
+    const int seg = blockIdx.x / parts, part = blockIdx.x % parts;
+    const int row = seg / heads, head = seg % heads;
+    const int j0 = int(int64_t(part) * nt / parts), j1 = int(int64_t(part + 1) * nt / parts);
+    const uint8_t* kh = k + size_t(row) * max_seq * row_bytes + head * 128;
+    const uint8_t* vh = v + size_t(row) * max_seq * row_bytes + head * 128;
+    const float* ksh = ks + (size_t(row) * heads + head) * max_seq;
+    const float* vsh = vs + (size_t(row) * heads + head) * max_seq;
+    for (int j = j0 + wave; j < j1; j += 4) {
+      q8_issue(stage, kh, vh, ksh, vsh, j * kQ8Tile, n_keys, row_bytes, lane);
+      acc ^= q8_use(stage, lane);
+    }
+  } else {
+    const int row = blockIdx.x / parts, part = blockIdx.x % parts;
+    const int j0 = int(int64_t(part) * nt / parts), j1 = int(int64_t(part + 1) * nt / parts);
+    for (int j = j0; j < j1; ++j)
+      for (int h = 2 * wave; h < 2 * wave + 2 && h < heads; ++h) {
+        const uint8_t* kh = k + size_t(row) * max_seq * row_bytes + h * 128;
+        const uint8_t* vh = v + size_t(row) * max_seq * row_bytes + h * 128;
+        q8_issue(stage, kh, vh, ks + (size_t(row) * heads + h) * max_seq, vs + (size_t(row) * heads + h) * max_seq,
+                 j * kQ8Tile, n_keys, row_bytes, lane);
+        acc ^= q8_use(stage, lane);
+      }
+  }
+  if (acc == kNeverXor) sink[0] = acc;
+}
+
+// Writes one 16-byte vector per thread (no loop): consecutive workgroups cover consecutive
+// 4 KB, so the stores in flight sweep the buffer in address order.
+__global__ __launch_bounds__(kThreads) void stream_write_kernel(uint8_t* __restrict__ buf, int64_t n16) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n16) reinterpret_cast<u32x4*>(buf)[i] = u32x4{uint32_t(i), 1u, 2u, 3u};
+}
+
 }  // namespace
 
 extern "C" int kvc_ceiling_stream_read(const void* buf, int64_t rows, int32_t row_bytes, int64_t stride_bytes,
@@ -211,5 +306,29 @@ extern "C" int kvc_ceiling_decode_read(const void* k, const void* v, int32_t row
   if (n_wg > 0x7fffffffLL || int64_t(n_keys) * parts > 0x7fffffffLL) return -1;
   hipLaunchKernelGGL(decode_read_kernel, dim3(unsigned(n_wg)), dim3(kThreads), 0, stream,
                      static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), n_keys, heads, parts, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" int kvc_ceiling_q8_read(const void* k, const void* v, const float* k_scale, const float* v_scale,
+                                   int32_t rows, int32_t n_keys, int32_t max_seq, int32_t heads, int32_t mode,
+                                   int32_t parts, uint32_t* sink, hipStream_t stream) {
+  if (!k || !v || !k_scale || !v_scale || !sink || rows < 1 || n_keys < 1 || max_seq < n_keys || heads < 1 ||
+      heads > 8 || parts < 1 || (mode != 0 && mode != 1) || (reinterpret_cast<uintptr_t>(k) & 15) != 0 ||
+      (reinterpret_cast<uintptr_t>(v) & 15) != 0)
+    return -1;
+  const int64_t n_wg = int64_t(rows) * (mode == 0 ? heads : 1) * parts;
+  if (n_wg > 0x7fffffffLL || int64_t(max_seq) * heads * 128 >= (int64_t(1) << 31)) return -1;
+  hipLaunchKernelGGL(q8_read_kernel, dim3(unsigned(n_wg)), dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), k_scale, v_scale, n_keys, max_seq,
+                     heads, mode, parts, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" int kvc_ceiling_stream_write(void* buf, int64_t bytes, hipStream_t stream) {
+  if (!buf || bytes < 16 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(buf) & 15) != 0) return -1;
+  const int64_t n16 = bytes / 16, wg = (n16 + kThreads - 1) / kThreads;
+  if (wg > 0x7fffffffLL) return -1;
+  hipLaunchKernelGGL(stream_write_kernel, dim3(unsigned(wg)), dim3(kThreads), 0, stream, static_cast<uint8_t*>(buf),
+                     n16);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }

@@ -84,6 +84,24 @@ def test_null_and_misaligned_pointers_rejected(ceil):
         assert lib.kvc_ceiling_decode_read(k, v, rows, keys, heads, parts, sink, None) == -1
 
 
+def test_q8_and_write_probes_reject_bad_arguments(ceil):
+    lib = ceil._load()
+    k, v, ks, vs, sink = (ctypes.c_void_p(a) for a in (0x10000, 0x40000, 0x80000, 0x90000, 0x20000))
+    ok = (4, 64, 64, 8, 0, 4)  # rows, n_keys, max_seq, heads, mode, parts
+    bad = [(0, 64, 64, 8, 0, 4), (4, 0, 64, 8, 0, 4), (4, 65, 64, 8, 0, 4), (4, 64, 64, 0, 0, 4),
+           (4, 64, 64, 9, 1, 4), (4, 64, 64, 8, 2, 4), (4, 64, 64, 8, 0, 0)]
+    for args in bad:
+        assert lib.kvc_ceiling_q8_read(k, v, ks, vs, *args, sink, None) == -1, args
+    assert lib.kvc_ceiling_q8_read(None, v, ks, vs, *ok, sink, None) == -1
+    assert lib.kvc_ceiling_q8_read(k, v, None, vs, *ok, sink, None) == -1
+    assert lib.kvc_ceiling_q8_read(k, v, ks, vs, *ok, None, None) == -1
+    assert lib.kvc_ceiling_q8_read(ctypes.c_void_p(0x10008), v, ks, vs, *ok, sink, None) == -1
+    assert lib.kvc_ceiling_stream_write(None, 4096, None) == -1
+    assert lib.kvc_ceiling_stream_write(ctypes.c_void_p(0x10000), 4100, None) == -1
+    assert lib.kvc_ceiling_stream_write(ctypes.c_void_p(0x10000), 0, None) == -1
+    assert lib.kvc_ceiling_stream_write(ctypes.c_void_p(0x10008), 4096, None) == -1
+
+
 @pytest.mark.gpu
 def test_measured_ceilings_are_plausible(ceil):
     import torch
@@ -110,3 +128,33 @@ def test_stream_read_counts_row_bytes(ceil):
     assert ceil.stream_read(buf, 512, 512, False, 8, sink) == 1 << 20
     torch.cuda.synchronize()
     assert int(sink.abs().sum()) == 0  # zeros fold to an XOR of 0, which never matches the sentinel
+
+
+@pytest.mark.gpu
+def test_q8_and_write_probes(ceil):
+    """The int8 read probes count 132 bytes per (key, head) for K and V each and read at a
+    plausible rate; the write probe writes every byte it is given and nothing past it."""
+    import torch
+
+    rows, max_seq, heads, n_keys = 2, 4100, 8, 4099  # a ragged last 32-key tile
+    g = torch.Generator(device="cuda").manual_seed(3)
+    k = torch.randint(-127, 128, (rows, max_seq, heads, 128), dtype=torch.int8, device="cuda", generator=g)
+    v = torch.randint(-127, 128, (rows, max_seq, heads, 128), dtype=torch.int8, device="cuda", generator=g)
+    ks = torch.rand(rows, heads, max_seq, device="cuda", generator=g)
+    vs = torch.rand(rows, heads, max_seq, device="cuda", generator=g)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for mode in (0, 1):
+        assert ceil.q8_read(k, v, ks, vs, n_keys, mode, 4, sink) == 2 * rows * n_keys * heads * 132
+    torch.cuda.synchronize()
+    r = ceil.measure_q8(k, v, ks, vs, n_keys, parts=(4, 16), reps=2)
+    assert all(10 < x < 8000 for x in r["q8_read_segments_gbps"].values())
+    assert 10 < r["q8_read_all_heads_gbps"]["value"] < 8000
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    assert ceil.stream_write(buf, (1 << 20) - 4096) == (1 << 20) - 4096
+    torch.cuda.synchronize()
+    words = buf.view(torch.int32).view(-1, 4)
+    n16 = ((1 << 20) - 4096) // 16
+    assert torch.equal(words[:n16, 0].cpu(), torch.arange(n16, dtype=torch.int32))
+    assert torch.equal(words[:n16, 1:].cpu(), torch.tensor([1, 2, 3], dtype=torch.int32).expand(n16, 3))
+    assert int(words[n16:].abs().sum()) == 0
+    assert 100 < ceil.measure_write(torch.empty(256 << 20, dtype=torch.uint8, device="cuda"), reps=2) < 8000
