@@ -957,12 +957,15 @@ def bench_clone(args):
     tok = 2 * hkv * d * 2
     nbytes = ctx * tok * (1 + rows)
     write_probe = None
-    if not args.no_ceilings:  # one contiguous buffer of the bytes the clone writes, written in address order
+    if not args.no_ceilings:  # the bytes the clone writes, with no read: in one run, and in its own rows
         from kv_cache_attention_kvcache_amd import ceilings
 
         wbuf = torch.empty(ctx * tok * rows, dtype=torch.uint8, device=dev)
-        write_probe = ceilings.measure_write(wbuf)
+        contiguous = ceilings.measure_write(wbuf, wbuf.numel())
         del wbuf
+        run, stride = ctx * tok // 2, w.max_seq * tok // 2  # one row's K (or V) positions, row to row
+        rk, rv = (ceilings.measure_write(t.view(torch.uint8).view(-1), run, rows, stride) for t in (dst.k, dst.v))
+        write_probe = {"contiguous": contiguous, "clone_rows": round(2 / (1 / rk + 1 / rv), 1)}
     med = lambda t: sorted(t.times_ms())[len(t.times_ms()) // 2]
     gbps = nbytes / (med(t_clone) * 1e-3) / 1e9
     fill_gbps = ctx * tok * rows / (med(t_fill) * 1e-3) / 1e9

@@ -40,7 +40,8 @@ def _load():
         lib.kvc_ceiling_decode_read.restype = ctypes.c_int
         lib.kvc_ceiling_q8_read.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 2
         lib.kvc_ceiling_q8_read.restype = ctypes.c_int
-        lib.kvc_ceiling_stream_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.kvc_ceiling_stream_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                                 ctypes.c_void_p]
         lib.kvc_ceiling_stream_write.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -120,14 +121,17 @@ def q8_read(k: torch.Tensor, v: torch.Tensor, k_scale: torch.Tensor, v_scale: to
     return 2 * rows * n_keys * heads * (128 + 4)
 
 
-def stream_write(buf: torch.Tensor, nbytes: int) -> int:
-    """Launch the streaming write over the first nbytes of buf (a contiguous uint8 device tensor)."""
-    if buf.dtype != torch.uint8 or not buf.is_cuda or not buf.is_contiguous() or nbytes > buf.numel():
-        raise ValueError("buf must be a contiguous uint8 device tensor of at least nbytes")
-    rc = _load().kvc_ceiling_stream_write(ctypes.c_void_p(buf.data_ptr()), nbytes, _stream_ptr())
+def stream_write(buf: torch.Tensor, run_bytes: int, rows: int = 1, stride_bytes: int = 0) -> int:
+    """Launch the streaming write of `rows` runs of run_bytes, stride_bytes apart, into buf (a
+    contiguous uint8 device tensor); returns the bytes written."""
+    need = (rows - 1) * stride_bytes + run_bytes
+    if buf.dtype != torch.uint8 or not buf.is_cuda or not buf.is_contiguous() or need > buf.numel():
+        raise ValueError(f"buf must be a contiguous uint8 device tensor of at least {need} bytes")
+    rc = _load().kvc_ceiling_stream_write(ctypes.c_void_p(buf.data_ptr()), run_bytes, rows, stride_bytes,
+                                          _stream_ptr())
     if rc != 0:
         raise RuntimeError(f"kvc_ceiling_stream_write failed ({rc})")
-    return nbytes
+    return rows * run_bytes
 
 
 def _timed(fn, reps: int) -> float:
@@ -242,8 +246,7 @@ def measure_q8(k: torch.Tensor, v: torch.Tensor, k_scale: torch.Tensor, v_scale:
     return {"q8_read_segments_gbps": seg, "q8_read_all_heads_gbps": {"value": max(allh.values()), "by_parts": allh}}
 
 
-def measure_write(buf: torch.Tensor, reps: int = 5) -> float:
-    """Rate (GB/s) of the streaming write over all of buf, one 16-byte store per thread."""
-    n = buf.numel() // 16 * 16
-    t = _timed(lambda: stream_write(buf, n), reps)
-    return round(n / t / 1e9, 1)
+def measure_write(buf: torch.Tensor, run_bytes: int, rows: int = 1, stride_bytes: int = 0, reps: int = 5) -> float:
+    """Rate (GB/s) of the streaming write of `rows` runs of run_bytes, stride_bytes apart, into buf."""
+    t = _timed(lambda: stream_write(buf, run_bytes, rows, stride_bytes), reps)
+    return round(rows * run_bytes / t / 1e9, 1)

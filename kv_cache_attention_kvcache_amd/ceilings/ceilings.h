@@ -67,9 +67,13 @@ int kvc_ceiling_q8_read(const void* k, const void* v, const float* k_scale, cons
                         int32_t n_keys, int32_t max_seq, int32_t heads, int32_t mode, int32_t parts, uint32_t* sink,
                         hipStream_t stream);
 
-// Writes `bytes` (a multiple of 16) of the 16-byte aligned device buffer, one 16-byte store
-// per thread, workgroups in address order.  Bytes written per call = bytes.
-int kvc_ceiling_stream_write(void* buf, int64_t bytes, hipStream_t stream);
+// Writes `rows` runs of `run_bytes` (a multiple of 16) into the 16-byte aligned device
+// buffer, run r starting at r * stride_bytes (a multiple of 16, at least run_bytes when
+// rows > 1), the buffer holding (rows - 1) * stride_bytes + run_bytes bytes.  Thread i
+// stores 16-byte vector i of every run (the prefill clone's write pattern without its
+// read); with rows = 1, a contiguous streaming write.  Bytes written per call =
+// rows * run_bytes.
+int kvc_ceiling_stream_write(void* buf, int64_t run_bytes, int32_t rows, int64_t stride_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

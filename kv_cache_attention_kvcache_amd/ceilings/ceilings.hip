@@ -252,11 +252,16 @@ __global__ __launch_bounds__(kThreads) void q8_read_kernel(const uint8_t* __rest
   if (acc == kNeverXor) sink[0] = acc;
 }
 
-// Writes one 16-byte vector per thread (no loop): consecutive workgroups cover consecutive
-// 4 KB, so the stores in flight sweep the buffer in address order.
-__global__ __launch_bounds__(kThreads) void stream_write_kernel(uint8_t* __restrict__ buf, int64_t n16) {
+// Writes `rows` runs of n16 16-byte vectors, run r starting r * stride16 vectors into buf.
+// Thread i writes vector i of every run in turn (no loop over i): consecutive workgroups
+// cover consecutive 4 KB of each run, so the stores in flight sweep every run in address
+// order -- with one run, a contiguous streaming write.
+__global__ __launch_bounds__(kThreads) void stream_write_kernel(uint8_t* __restrict__ buf, int64_t n16, int32_t rows,
+                                                                int64_t stride16) {
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (i < n16) reinterpret_cast<u32x4*>(buf)[i] = u32x4{uint32_t(i), 1u, 2u, 3u};
+  if (i >= n16) return;
+  for (int r = 0; r < rows; ++r)
+    reinterpret_cast<u32x4*>(buf)[r * stride16 + i] = u32x4{uint32_t(i), uint32_t(r), 2u, 3u};
 }
 
 }  // namespace
@@ -324,11 +329,14 @@ extern "C" int kvc_ceiling_q8_read(const void* k, const void* v, const float* k_
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
-extern "C" int kvc_ceiling_stream_write(void* buf, int64_t bytes, hipStream_t stream) {
-  if (!buf || bytes < 16 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(buf) & 15) != 0) return -1;
-  const int64_t n16 = bytes / 16, wg = (n16 + kThreads - 1) / kThreads;
+extern "C" int kvc_ceiling_stream_write(void* buf, int64_t run_bytes, int32_t rows, int64_t stride_bytes,
+                                        hipStream_t stream) {
+  if (!buf || run_bytes < 16 || run_bytes % 16 != 0 || rows < 1 || stride_bytes % 16 != 0 ||
+      (rows > 1 && stride_bytes < run_bytes) || (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+    return -1;
+  const int64_t n16 = run_bytes / 16, wg = (n16 + kThreads - 1) / kThreads;
   if (wg > 0x7fffffffLL) return -1;
   hipLaunchKernelGGL(stream_write_kernel, dim3(unsigned(wg)), dim3(kThreads), 0, stream, static_cast<uint8_t*>(buf),
-                     n16);
+                     n16, rows, stride_bytes / 16);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }

@@ -96,10 +96,14 @@ def test_q8_and_write_probes_reject_bad_arguments(ceil):
     assert lib.kvc_ceiling_q8_read(k, v, None, vs, *ok, sink, None) == -1
     assert lib.kvc_ceiling_q8_read(k, v, ks, vs, *ok, None, None) == -1
     assert lib.kvc_ceiling_q8_read(ctypes.c_void_p(0x10008), v, ks, vs, *ok, sink, None) == -1
-    assert lib.kvc_ceiling_stream_write(None, 4096, None) == -1
-    assert lib.kvc_ceiling_stream_write(ctypes.c_void_p(0x10000), 4100, None) == -1
-    assert lib.kvc_ceiling_stream_write(ctypes.c_void_p(0x10000), 0, None) == -1
-    assert lib.kvc_ceiling_stream_write(ctypes.c_void_p(0x10008), 4096, None) == -1
+    buf = ctypes.c_void_p(0x10000)
+    assert lib.kvc_ceiling_stream_write(None, 4096, 1, 0, None) == -1
+    assert lib.kvc_ceiling_stream_write(buf, 4100, 1, 0, None) == -1           # not whole vectors
+    assert lib.kvc_ceiling_stream_write(buf, 0, 1, 0, None) == -1
+    assert lib.kvc_ceiling_stream_write(ctypes.c_void_p(0x10008), 4096, 1, 0, None) == -1
+    assert lib.kvc_ceiling_stream_write(buf, 4096, 0, 8192, None) == -1         # no runs
+    assert lib.kvc_ceiling_stream_write(buf, 4096, 2, 2048, None) == -1         # runs overlap
+    assert lib.kvc_ceiling_stream_write(buf, 4096, 2, 8200, None) == -1         # stride not whole vectors
 
 
 @pytest.mark.gpu
@@ -152,9 +156,23 @@ def test_q8_and_write_probes(ceil):
     buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
     assert ceil.stream_write(buf, (1 << 20) - 4096) == (1 << 20) - 4096
     torch.cuda.synchronize()
-    words = buf.view(torch.int32).view(-1, 4)
+    words = buf.view(torch.int32).view(-1, 4).cpu()
     n16 = ((1 << 20) - 4096) // 16
-    assert torch.equal(words[:n16, 0].cpu(), torch.arange(n16, dtype=torch.int32))
-    assert torch.equal(words[:n16, 1:].cpu(), torch.tensor([1, 2, 3], dtype=torch.int32).expand(n16, 3))
+    assert torch.equal(words[:n16, 0], torch.arange(n16, dtype=torch.int32))
+    assert torch.equal(words[:n16, 1:], torch.tensor([0, 2, 3], dtype=torch.int32).expand(n16, 3))
     assert int(words[n16:].abs().sum()) == 0
-    assert 100 < ceil.measure_write(torch.empty(256 << 20, dtype=torch.uint8, device="cuda"), reps=2) < 8000
+    # three runs of 80,016 bytes (a ragged last workgroup) at a 262,144-byte stride: only those bytes change
+    buf.zero_()
+    run, stride = 80016, 1 << 18
+    assert ceil.stream_write(buf, run, 3, stride) == 3 * run
+    torch.cuda.synchronize()
+    words = buf.view(torch.int32).view(-1, 4).cpu()
+    want = torch.zeros_like(words)
+    for r in range(3):
+        v0 = r * stride // 16
+        want[v0:v0 + run // 16, 0] = torch.arange(run // 16, dtype=torch.int32)
+        want[v0:v0 + run // 16, 1:] = torch.tensor([r, 2, 3], dtype=torch.int32)
+    assert torch.equal(words, want)
+    big = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    assert 100 < ceil.measure_write(big, big.numel(), reps=2) < 8000
+    assert 100 < ceil.measure_write(big, 16 << 20, 8, 32 << 20, reps=2) < 8000
