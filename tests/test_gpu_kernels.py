@@ -373,6 +373,33 @@ def test_prefill_matches_oracle(kvc, dtype, hq, hkv, d, t_len, start):
         gates.check(o[b], ref, dtype, f"prefill row {b} start {s}")
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,d,t_len", [("bf16", 16, 4, 128, 300), ("bf16", 64, 8, 128, 257),
+                                                   ("f32", 8, 2, 64, 33)])
+def test_prefill_fills_the_cache_exactly(kvc, dtype, hq, hkv, d, t_len):
+    """Rows whose chunk ends exactly at max_seq (start + T == max_seq, the last slot the capacity
+    check allows): every key up to the last slot is attended, nothing past the cache is read."""
+    g = _rng(9, hq, d, t_len)
+    starts = [131, 0]
+    max_seq = max(starts) + t_len
+    cache = make_cache(kvc, 1, 2, max_seq, hkv, d, dtype)
+    hist_k, hist_v = _fill_prefix(cache, 0, starts, dtype, g)
+    q = g.standard_normal((2, t_len, hq, d)).astype(np.float32)
+    k = g.standard_normal((2, t_len, hkv, d)).astype(np.float32)
+    v = g.standard_normal((2, t_len, hkv, d)).astype(np.float32)
+    q_rot = kvc.kvc_rope_append(cache, 0, dev(q, dtype), dev(k, dtype), dev(v, dtype))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = kvc.kvc_attn_prefill(cache, 0, q_rot, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    o = host64(out)
+    for b, s in enumerate(starts):
+        k_new, v_new = oatt.appended_slots(k[b], v[b], s, dtype)
+        ka = np.concatenate([hist_k[b], k_new])
+        va = np.concatenate([hist_v[b], v_new])
+        qh = rope.rotate_round(numerics.round_to(q[b], dtype), np.arange(s, s + t_len), dtype)
+        gates.check(o[b], oatt.attend(qh, ka, va, np.arange(s, s + t_len)), dtype, f"row {b} start {s}")
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(64, 8, 128), (64, 16, 64)])
 def test_prefill_four_and_eight_wave_forms_agree(kvc, hq, hkv, d):
     """A batch of 8 rows at 64 query heads takes the 8-wave prefill (its grid fills the device);
