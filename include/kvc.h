@@ -28,8 +28,9 @@
  * the Cache Change the Output?": the cache keeps the last max_seq positions,
  * each rotated at its absolute position; under RoPE a score is a function of
  * how far apart the two positions are, not of where they sit, so the window
- * can slide without rotating any cached key again.  seqlens[b] then counts every token row b has seen, and
- * absolute position p lives in slot p mod max_seq.  kvc_rope_append writes
+ * can slide without rotating any cached key again.  seqlens[b] then counts
+ * every token row b has seen, and absolute position p lives in slot
+ * p mod max_seq.  kvc_rope_append writes
  * token t at slot (P + t) mod max_seq (T <= max_seq, else KVC_E_ARG), rotated
  * at P + t; a one-token decode (kvc_attn_decode, kvc_decode_step) attends the
  * min(P + 1, max_seq) filled slots -- positions max(0, P + 1 - max_seq) .. P,
@@ -111,7 +112,7 @@ typedef struct kvc_cache {
   int32_t dtype;    /* KVC_F32, KVC_BF16 or KVC_I8 */
   float* k_scale;   /* KVC_I8 only: device, (n_layers, batch, n_kv_heads, max_seq); else ignored */
   float* v_scale;   /* KVC_I8 only: device, same shape */
-  int32_t rolling;  /* 0: linear cache; 1: rolling window of max_seq positions (see below) */
+  int32_t rolling;  /* 0: linear cache; 1: rolling window of max_seq positions (see above) */
 } kvc_cache;
 
 /*
@@ -164,10 +165,11 @@ size_t kvc_decode_workspace_bytes(const kvc_cache* cache, int32_t n_q_heads, int
  *          kvc_rope_append).
  *   out    device, same shape as q_rot.
  *   scale  softmax scale; <= 0 selects 1/sqrt(head_dim).
- *   n_workers  bfloat16 caches: the number of workgroups the cached keys of
- *          all rows are split evenly over (split-KV); 0 = one per compute
- *          unit of the current device.  Float32 caches use fixed 512-key splits and
- *          ignore it.  A result depends on the lengths of all rows and on
+ *   n_workers  bfloat16 and int8 caches: the number of workgroups the cached
+ *          keys of all rows are split evenly over (split-KV); 0 = one per
+ *          compute unit of the current device.  Float32 caches use fixed
+ *          512-key splits and ignore it.  A result depends on the lengths of
+ *          all rows and on
  *          n_workers only through the order of float32 additions; it is
  *          bit-identical run to run for the same inputs and n_workers.
  *   workspace   device scratch of at least kvc_decode_workspace_bytes bytes,
