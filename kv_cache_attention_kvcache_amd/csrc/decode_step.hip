@@ -18,6 +18,10 @@
 //      LDS); for the weighted sum of V wave w takes every fourth key of the
 //      tile and lane l the head dims l, l + 64, for all G heads at once; the
 //      four waves' sums are added in a fixed order at the end.
+// The kernel is bound by memory latency, not bandwidth: a key's V load is
+// issued in chunks of 16 per lane before any of them is used (a loop that
+// loads and uses one key per iteration waits for every load in turn: 64
+// round trips per tile instead of 4), and a key row's loads all at once.
 // The slot this workgroup wrote is read back by it after a barrier.
 #include "kvc_device.h"
 #include "kvc_launch.h"
@@ -30,6 +34,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 256;  // keys per tile: one per thread
 constexpr int kWaves = kThreads / kWave;
+constexpr int kVChunk = 16;  // V loads in flight per lane in the weighted sum (kVChunk * kWaves divides kTile)
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16_t x) { return bf16_to_f32(x); }
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeStepParams 
     for (int h = 0; h < GB; ++h) s[h] = 0.f;
     if (j < n_keys) {
       const T* krow = k_base + size_t(j) * key_stride;
-#pragma unroll 4
+#pragma unroll
       for (int d0 = 0; d0 < D; d0 += 8) {
         float kx[8];
         load8(krow + d0, kx);
@@ -191,18 +196,28 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeStepParams 
     for (int h = 0; h < GB; ++h)
 #pragma unroll
       for (int u = 0; u < kDU; ++u) acc[h][u] *= alpha[h];
+    // The chunk's kVChunk loads are issued back to back before any is used: a
+    // key past the tile's last is read at the last key's index (a filled slot)
+    // and weighted by its probability, 0.  i stays below kTile.
     const T* vrow = v_base + size_t(j0) * key_stride + lane;
-#pragma unroll 4
-    for (int i = wave; i < n_in; i += kWaves) {
-      float vv[kDU];
+    for (int i0 = wave; i0 < n_in; i0 += kVChunk * kWaves) {
+      float vv[kVChunk][kDU];
 #pragma unroll
-      for (int u = 0; u < kDU; ++u) vv[u] = to_f(vrow[size_t(i) * key_stride + kWave * u]);
+      for (int c = 0; c < kVChunk; ++c) {
+        const int ic = min(i0 + kWaves * c, n_in - 1);
 #pragma unroll
-      for (int h = 0; h < GB; ++h) {
-        if (h < G) {
-          const float ph = pr[h][i];
+        for (int u = 0; u < kDU; ++u) vv[c][u] = to_f(vrow[size_t(ic) * key_stride + kWave * u]);
+      }
 #pragma unroll
-          for (int u = 0; u < kDU; ++u) acc[h][u] = fmaf(ph, vv[u], acc[h][u]);
+      for (int c = 0; c < kVChunk; ++c) {
+        const int i = i0 + kWaves * c;
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+          if (h < G) {
+            const float ph = pr[h][i];
+#pragma unroll
+            for (int u = 0; u < kDU; ++u) acc[h][u] = fmaf(ph, vv[c][u], acc[h][u]);
+          }
         }
       }
     }
