@@ -964,6 +964,28 @@ __global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p
            range_begin(w_first + i, n_tiles, p.n_wg) == range_begin(w_first + i + 1LL, n_tiles, p.n_wg);
   };
 
+  // This thread folds partials pi, pi + kPI, ... (16 bytes of each o row).  Their
+  // loads are issued kCh at a time before any is used -- the first kCh before
+  // the maximum pass, so both passes wait for memory once -- because a loop
+  // that loads and uses one partial per iteration waits for every load in
+  // turn.  A slot past the last partial is read at the last one's index and
+  // not used.
+  const int ck = threadIdx.x % kChunks;
+  const int pi = threadIdx.x / kChunks;
+  constexpr int kCh = 8;
+  float4 ov[kCh];
+  float mv[kCh], lv[kCh];
+  auto fetch = [&](int i0) {
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+      const size_t ps = part(min(i0 + kPI * c, count - 1));
+      mv[c] = p.ws_ml[ps * 2];
+      lv[c] = p.ws_ml[ps * 2 + 1];
+      ov[c] = *reinterpret_cast<const float4*>(p.ws_o + ps * D + 4 * ck);
+    }
+  };
+  fetch(pi);
+
   float mx = -INFINITY;
   for (int i = threadIdx.x; i < count; i += blockDim.x)
     if (!empty(i)) mx = fmaxf(mx, p.ws_ml[part(i) * 2]);
@@ -972,17 +994,18 @@ __global__ __launch_bounds__(256) void decode_bf16_combine_kernel(DecodeParams p
   __syncthreads();
   const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
 
-  const int ck = threadIdx.x % kChunks;
-  const int pi = threadIdx.x / kChunks;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
-  for (int i = pi; i < count; i += kPI) {
-    if (empty(i)) continue;
-    const size_t ps = part(i);
-    const float f = exp2f(p.ws_ml[ps * 2] - M);
-    const float4 o = *reinterpret_cast<const float4*>(p.ws_o + ps * D + 4 * ck);
-    a.x += f * o.x; a.y += f * o.y; a.z += f * o.z; a.w += f * o.w;
-    den += f * p.ws_ml[ps * 2 + 1];
+  for (int i0 = pi; i0 < count; i0 += kCh * kPI) {
+    if (i0 != pi) fetch(i0);
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+      const int i = i0 + kPI * c;
+      if (i >= count || empty(i)) continue;
+      const float f = exp2f(mv[c] - M);
+      a.x += f * ov[c].x; a.y += f * ov[c].y; a.z += f * ov[c].z; a.w += f * ov[c].w;
+      den += f * lv[c];
+    }
   }
   *reinterpret_cast<float4*>(&red[pi][4 * ck]) = a;
   if (ck == 0) red_l[pi] = den;
