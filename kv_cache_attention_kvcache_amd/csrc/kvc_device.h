@@ -42,10 +42,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 
 // One RoPE pair rotation in float32 (half-split pairs i and i + D/2):
 // (x, y) -> (x c - y s, x s + y c).  Every kernel that rotates uses this one
-// expression, so that they all round the same way.
+// function, so that they all round the same way.  The fused multiply-adds are
+// written out: left as x * c - y * s, which product the compiler fuses may
+// differ from one call site (or unrolled copy) to another, and with it the
+// last bit of the result.
 __device__ __forceinline__ void rope_pair(float x, float y, float c, float s, float& xr, float& yr) {
-  xr = x * c - y * s;
-  yr = x * s + y * c;
+  xr = fmaf(x, c, -(y * s));
+  yr = fmaf(x, s, y * c);
 }
 
 // Byte permute: pick bytes of {hi_src:lo_src} (lo_src = bytes 0..3, hi_src = bytes 4..7).
