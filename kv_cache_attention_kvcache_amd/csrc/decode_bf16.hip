@@ -356,8 +356,11 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
       }
     };
 
-    // Tile j: K in kb (two register stages, the next K tile always in flight),
-    // V in vb (one stage: the next V tile is issued as soon as this one is in LDS).
+    // Tile j: K in kb and V in vb, one register stage each: the wave's next K
+    // tile is issued as soon as this one's dots are formed, its next V tile as
+    // soon as this one is in LDS.  (A second K stage, keeping two K tiles in
+    // flight, streamed about 2% slower: more partial-row requests in flight
+    // cost the memory side more than they hide.)
     // k_next / v_next: tiles to issue into kb / vb once they are consumed (-1: none).
     auto process = [&](int j, Raw* kb, float* ksb, Raw* vb, float* vsb, int k_next, int v_next) {
       // ---- partial dots of slot s against the GB queries, then the head-splitting
@@ -501,27 +504,17 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_bf16_kernel(DecodePa
     };
 
     // The wave's tiles of this run: j0 + wave, j0 + wave + 4, ...
-    Raw kA[C::NR], kB[C::NR], vb[C::NR];
-    float ksA[C::NRK], ksB[C::NRK], vsb[C::NRK];
+    Raw kb[C::NR], vb[C::NR];
+    float ksb[C::NRK], vsb[C::NRK];
     int j = j0 + wave;
     if (j < j1) {
-      issue(kseg, j, kA);
-      issue_sc(ksseg, j, ksA);
+      issue(kseg, j, kb);
+      issue_sc(ksseg, j, ksb);
       issue(vseg, j, vb);
       issue_sc(vsseg, j, vsb);
-      if (j + kWaves < j1) {
-        issue(kseg, j + kWaves, kB);
-        issue_sc(ksseg, j + kWaves, ksB);
-      }
     }
     auto next = [&](int jj) { return jj < j1 ? jj : -1; };
-    while (j < j1) {
-      process(j, kA, ksA, vb, vsb, next(j + 2 * kWaves), next(j + kWaves));
-      j += kWaves;
-      if (j >= j1) break;
-      process(j, kB, ksB, vb, vsb, next(j + 2 * kWaves), next(j + kWaves));
-      j += kWaves;
-    }
+    for (; j < j1; j += kWaves) process(j, kb, ksb, vb, vsb, next(j + kWaves), next(j + kWaves));
 
     // ---- fold the four waves' states of this run
     // sum of head ghx over the lanes that hold it (row-splitting partners, then row groups)
