@@ -151,6 +151,53 @@ def test_clone_is_bit_exact(kvc, dtype, hkv, d):
     assert np.array_equal(dv[:, :, src_len:], before_v[:, :, src_len:])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "int8"])
+def test_clone_of_an_empty_prompt_and_to_one_row(kvc, dtype):
+    """Degenerate clones: src_len = 0 copies nothing, reports nothing and leaves the
+    destination rows empty (seqlens 0); a batch-1 destination gets the one copy."""
+    hkv, d = 4, 128
+    src = make_cache(kvc, 2, 1, 64, hkv, d, "bf16", poison=False)
+    src.k.normal_()
+    src.v.normal_()
+    if dtype == "int8":
+        src = kvc.KVCache.empty(2, 1, 64, hkv, d, dtype=torch.int8)
+        src.k.random_(-127, 128)
+        src.v.random_(-127, 128)
+        src.k_scale.uniform_()
+        src.v_scale.uniform_()
+
+    def dest(batch):
+        if dtype == "int8":
+            c = kvc.KVCache.empty(2, batch, 64, hkv, d, dtype=torch.int8)
+            for t in (c.k, c.v):
+                t.fill_(0x55)
+            for t in (c.k_scale, c.v_scale):
+                t.fill_(-1.0)
+            return c
+        return make_cache(kvc, 2, batch, 64, hkv, d, "bf16")
+
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    src.seqlens.fill_(0)
+    dst = dest(3)
+    before = [bits(t) for t in (dst.k, dst.v)] + ([host64(dst.k_scale)] if dtype == "int8" else [])
+    kvc.kvc_prefill_clone(src, 0, dst, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and dst.seqlens.cpu().tolist() == [0, 0, 0]
+    assert np.array_equal(bits(dst.k), before[0]) and np.array_equal(bits(dst.v), before[1])
+    if dtype == "int8":
+        assert np.array_equal(host64(dst.k_scale), before[2])
+    src.seqlens.fill_(17)
+    one = dest(1)
+    kvc.kvc_prefill_clone(src, 17, one, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and one.seqlens.cpu().tolist() == [17]
+    assert np.array_equal(bits(one.k)[:, 0, :17], bits(src.k)[:, 0, :17])
+    assert np.array_equal(bits(one.v)[:, 0, :17], bits(src.v)[:, 0, :17])
+    if dtype == "int8":
+        assert np.array_equal(host64(one.k_scale)[:, 0, :, :17], host64(src.k_scale)[:, 0, :, :17])
+        assert np.all(host64(one.k_scale)[:, 0, :, 17:] == -1.0)
+
+
 def test_clone_errors(kvc):
     dtype = "bf16"
     src = make_cache(kvc, 2, 1, 64, 4, 128, dtype, poison=False)
