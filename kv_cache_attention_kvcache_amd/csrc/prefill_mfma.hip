@@ -21,8 +21,16 @@
 //     straight from the score registers rounded to bfloat16.
 //   * Only tiles that reach past a wave's first query position are masked;
 //     fully hidden tiles are never loaded.  P*V of the previous tile runs
-//     beside the softmax of the current one.  The next tile's K/V is fetched
+//     beside the softmax of the current one.  The next tile's V is fetched
 //     into registers while the current one is computed.
+//   * At head_dim 128 the K tiles skip the registers: buffer loads write them
+//     straight into one of four LDS buffers, two tiles ahead, with the 16-byte
+//     chunks of each row XOR-swizzled by the row index so the MFMA operand
+//     reads stay conflict-free without padding (a DMA fills LDS contiguously).
+//     Each step then needs one barrier, and the waits on those loads are
+//     written out (vmcnt with lgkmcnt), since the fence of __syncthreads would
+//     wait for every load in flight, the next tiles' included.  Other head
+//     sizes stage K through registers into two padded buffers.
 //   * Workgroups are ordered so that the query heads sharing a KV head run
 //     on the same XCD (its L2 serves their common K/V stream), longest
 //     (latest) query tiles first.
@@ -30,6 +38,7 @@
 //     own token count and first packed row; the grid covers the largest count
 //     and workgroups past a row's tokens, or of rows with fewer than two
 //     tokens, return at once.
+#include <type_traits>
 #include "kvc_device.h"
 #include "kvc_launch.h"
 #include "kvc.h"
@@ -72,7 +81,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void prefill_mfma_kernel(PrefillPara
   constexpr int kKD = D / 16;                 // MFMA k-steps over the head dim
   constexpr int kDB = D / 32;                 // 32-dim output blocks
   constexpr int kKLoads = kBN * D * 2 / 16 / kThreads;  // 16-byte K loads per thread per tile
-  __shared__ __align__(16) uint8_t k_lds[2][kBN * kKStride];  // K tiles, two buffers
+  // head_dim 128: K goes from memory straight into LDS (buffer_load ... lds), four buffers,
+  // 16-byte chunks XOR-swizzled per row; otherwise register-staged into two padded buffers.
+  constexpr bool kDma = D == 128;
+  constexpr int kDmaBytes = kBN * D * 2;
+  __shared__ __align__(16) uint8_t k_lds[kDma ? 1 : 2][kDma ? 16 : kBN * kKStride];
+  __shared__ __align__(16) uint8_t k_dma0[kDma ? kDmaBytes : 16], k_dma1[kDma ? kDmaBytes : 16],
+      k_dma2[kDma ? kDmaBytes : 16], k_dma3[kDma ? kDmaBytes : 16];
   __shared__ __align__(16) uint8_t v_lds[2][D * kVStride];    // V^T tiles, two buffers
 
   const int hq = p.n_q_heads;
@@ -224,14 +239,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void prefill_mfma_kernel(PrefillPara
 
   // S^T of one tile: 2 blocks of 32 keys, the first k-step from a zero accumulator.
   // All 16 K fragments are read first; the two blocks' chains alternate.
-  auto qk = [&](int buf, f32x16_t* s) {
+  auto qk_from = [&](const uint8_t* kbase, f32x16_t* s) {
     uint4 kf[2 * kKD];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kd = 0; kd < kKD; ++kd)
+      for (int kd = 0; kd < kKD; ++kd) {
+        const int r = 32 * kb + arow;
         kf[kb * kKD + kd] =
-            *reinterpret_cast<const uint4*>(k_lds[buf] + (32 * kb + arow) * kKStride + 16 * half + 32 * kd);
+            kDma ? *reinterpret_cast<const uint4*>(kbase + (r * 16 + ((2 * kd + half) ^ (r & 15))) * 16)
+                 : *reinterpret_cast<const uint4*>(kbase + r * kKStride + 16 * half + 32 * kd);
+      }
 #pragma unroll
     for (int kd = 0; kd < kKD; ++kd)
 #pragma unroll
@@ -242,6 +260,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void prefill_mfma_kernel(PrefillPara
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKD, 0);  // every K fragment read first
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * kKD, 0);  // then the score MFMAs
   };
+  auto qk = [&](int buf, f32x16_t* s) { qk_from(k_lds[buf], s); };
   // Keys past a query's position get score -inf.  Only tiles that reach past
   // the wave's first query need it; a tile wholly past every query of the wave
   // masks to -inf throughout and contributes exact zeros.
@@ -355,6 +374,82 @@ __global__ __launch_bounds__(64 * WAVES, 1) void prefill_mfma_kernel(PrefillPara
     soft(s, pf_cur);
     __syncthreads();
   };
+  if constexpr (kDma) {
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    constexpr int kKDma = kDmaBytes / 16 / kThreads;  // 1 KB DMA instructions per wave per tile
+    constexpr int kVLoads = 2 * kVPer;                  // V loads per thread per tile
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto dma_k = [&](int tile, uint8_t* dst) {
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k_base, tile * kBN);
+#pragma unroll
+      for (int i = 0; i < kKDma; ++i) {
+        const int blk = i * WAVES + wave_u;  // this instruction's 1 KB of the tile in LDS
+        const int pch = blk * 64 + lane;     // LDS chunk the lane's 16 bytes land in
+        const int r = pch >> 4;
+        const int c = (pch & 15) ^ (r & 15);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(dst + blk * 1024), 16, r * row_bytes + c * 16, 0, 0, 0);
+      }
+    };
+    // vmcnt(vm) with lgkmcnt(0): every LDS access of this wave done, and all but its vm latest
+    // vector memory instructions.
+    auto wait_vm = [&](auto vmc) {
+      constexpr int vm = decltype(vmc)::value;
+      __builtin_amdgcn_s_waitcnt((vm & 0xF) | ((vm >> 4) << 14) | (7 << 4));
+    };
+    auto barrier = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    uint4 pa[4], pb[4];
+    dma_k(0, k_dma0);
+    dma_k(1, k_dma1);
+    load_v(0);
+    wait_vm(std::integral_constant<int, 0>{});
+    store_v(0);
+    load_v(1);
+    dma_k(2, k_dma2);
+    wait_vm(std::integral_constant<int, kKDma + kVLoads>{});
+    barrier();
+    {
+      f32x16_t s[2];
+      qk_from(k_dma0, s);
+      mask(0, s);
+      soft(s, pa);
+    }
+    wait_vm(std::integral_constant<int, kKDma + kVLoads>{});
+    barrier();  // every wave has read K(0) before K(4) lands in its buffer
+    // Step j: K(j) in kc, K(j+1) landed or in flight, V(j) in registers, V(j-1) in v_lds.
+    auto dstep = [&](int j, const uint8_t* kc, uint8_t* kn2, const uint4* pf_prev, uint4* pf_cur) {
+      f32x16_t s[2];
+      uint4 vf[4 * kDB];
+      qk_from(kc, s);
+      store_v(j & 1);
+      dma_k(j + 2, kn2);
+      load_v(j + 1);
+      read_v((j - 1) & 1, vf);
+      mask(j, s);
+      pv(vf, pf_prev);
+      soft(s, pf_cur);
+      wait_vm(std::integral_constant<int, kKDma + kVLoads>{});  // K(j+1) has landed
+      barrier();
+    };
+    int j = 1;
+    for (; j + 3 < n_tiles; j += 4) {
+      dstep(j, k_dma1, k_dma3, pa, pb);
+      dstep(j + 1, k_dma2, k_dma0, pb, pa);
+      dstep(j + 2, k_dma3, k_dma1, pa, pb);
+      dstep(j + 3, k_dma0, k_dma2, pb, pa);
+    }
+    if (j < n_tiles) dstep(j, k_dma1, k_dma3, pa, pb);
+    if (j + 1 < n_tiles) dstep(j + 1, k_dma2, k_dma0, pb, pa);
+    if (j + 2 < n_tiles) dstep(j + 2, k_dma3, k_dma1, pa, pb);
+    {
+      uint4 vf[4 * kDB];
+      read_v((n_tiles - 1) & 1, vf);
+      pv(vf, ((n_tiles - 1) & 1) ? pb : pa);
+    }
+  } else {
   load_k(0);
   load_v(0);
   store_k(0);
@@ -382,6 +477,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void prefill_mfma_kernel(PrefillPara
     uint4 vf[4 * kDB];
     read_v((n_tiles - 1) & 1, vf);
     pv(vf, ((n_tiles - 1) & 1) ? pb : pa);
+  }
   }
 
   // ---- normalise and store: o[db] register r holds head dim 32 db + 8 (r >> 2) + 4 half + (r & 3).
