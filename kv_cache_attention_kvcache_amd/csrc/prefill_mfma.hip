@@ -27,6 +27,8 @@
 //     straight into one of four LDS buffers, two tiles ahead, with the 16-byte
 //     chunks of each row XOR-swizzled by the row index so the MFMA operand
 //     reads stay conflict-free without padding (a DMA fills LDS contiguously).
+//     The four buffers are one array, so a lane's eight swizzled read
+//     addresses serve every buffer and block through the instruction offset.
 //     Each step then needs one barrier, and the waits on those loads are
 //     written out (vmcnt with lgkmcnt), since the fence of __syncthreads would
 //     wait for every load in flight, the next tiles' included.  Other head
@@ -86,8 +88,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void prefill_mfma_kernel(PrefillPara
   constexpr bool kDma = D == 128;
   constexpr int kDmaBytes = kBN * D * 2;
   __shared__ __align__(16) uint8_t k_lds[kDma ? 1 : 2][kDma ? 16 : kBN * kKStride];
-  __shared__ __align__(16) uint8_t k_dma0[kDma ? kDmaBytes : 16], k_dma1[kDma ? kDmaBytes : 16],
-      k_dma2[kDma ? kDmaBytes : 16], k_dma3[kDma ? kDmaBytes : 16];
+  __shared__ __align__(16) uint8_t k_dma[kDma ? 4 * kDmaBytes : 16];
+  uint8_t* const k_dma0 = k_dma;
+  uint8_t* const k_dma1 = k_dma + (kDma ? kDmaBytes : 0);
+  uint8_t* const k_dma2 = k_dma + (kDma ? 2 * kDmaBytes : 0);
+  uint8_t* const k_dma3 = k_dma + (kDma ? 3 * kDmaBytes : 0);
   __shared__ __align__(16) uint8_t v_lds[2][D * kVStride];    // V^T tiles, two buffers
 
   const int hq = p.n_q_heads;
