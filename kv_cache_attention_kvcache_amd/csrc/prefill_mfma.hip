@@ -449,6 +449,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void prefill_mfma_kernel(PrefillPara
     if (j < n_tiles) dstep(j, k_dma1, k_dma3, pa, pb);
     if (j + 1 < n_tiles) dstep(j + 1, k_dma2, k_dma0, pb, pa);
     if (j + 2 < n_tiles) dstep(j + 2, k_dma3, k_dma1, pa, pb);
+    // The last steps issued loads of tiles past the end (no memory is read for them); none
+    // may still be writing this workgroup's LDS when it exits.
+    wait_vm(std::integral_constant<int, 0>{});
     {
       uint4 vf[4 * kDB];
       read_v((n_tiles - 1) & 1, vf);
