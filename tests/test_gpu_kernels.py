@@ -388,6 +388,8 @@ PREFILL_CASES = [  # (dtype, Hq, Hkv, D, T, start)
     ("bf16", 16, 4, 128, 129, 0),
     ("bf16", 16, 4, 128, 300, 77),
     ("bf16", 64, 8, 128, 64, 1000),
+    ("bf16", 8, 1, 128, 150, 40),    # one KV head: 256-byte K rows
+    ("bf16", 32, 32, 128, 100, 5),   # no head sharing: 8 KiB K rows
     ("bf16", 8, 8, 64, 200, 0),
     ("bf16", 12, 4, 64, 131, 129),
     ("f32", 4, 4, 64, 8, 0),
